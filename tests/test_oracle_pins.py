@@ -1,0 +1,348 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped ReLU, the weight
+inside the ReLU, an off-by-one mask, a reversed tie-break, a transposed operand, a
+wrong E4M3 exponent bias, a missing key scale) fails at least one of them;
+``test_planted_mistakes_are_caught`` plants each slip and checks exactly that.
+"""
+
+from __future__ import annotations
+
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.indexer as OI
+import synth
+from hand import bits, build, expected, load_cases
+
+CASES = load_cases()
+
+
+# ---------------------------------------------------------------------------
+# Hand-built cases (tests/golden/hand_cases.json)
+# ---------------------------------------------------------------------------
+
+def _run_hand(case):
+    x = build(case)
+    return oracle.indexer_topk(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), x["m"], x["k"],
+                               kc_dtype=x["kc_dtype"],
+                               kc_scale=None if x["kc_scale"] is None else x["kc_scale"].numpy(),
+                               q_pos0=x["q_pos0"])
+
+
+def _check_hand(case):
+    idx, val = _run_hand(case)
+    eidx, evals = expected(case)
+    np.testing.assert_array_equal(idx, eidx, err_msg=case["name"])
+    np.testing.assert_array_equal(val, evals, err_msg=case["name"])
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_hand_case(case):
+    _check_hand(case)
+
+
+# ---------------------------------------------------------------------------
+# Exact rational brute force on tiny random inputs (pure Python loops)
+# ---------------------------------------------------------------------------
+
+def _bf16_exact(v: float) -> Fraction:
+    return Fraction(float(torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).float()))
+
+
+def _brute_force(qv, kv, wv, m, k, q_pos0):
+    """Exact scores with Fractions, exact ties, sort by (score desc, index asc)."""
+    S, H, D = len(qv), len(qv[0]), len(qv[0][0])
+    T = len(kv)
+    out = []
+    for t in range(S):
+        vis = [s for s in range(T) if (s + 1) * m <= q_pos0 + t + 1]
+        sc = []
+        for s in vis:
+            tot = Fraction(0)
+            for h in range(H):
+                dot = sum((qv[t][h][d] * kv[s][d] for d in range(D)), Fraction(0))
+                tot += wv[t][h] * max(dot, Fraction(0))
+            sc.append((-tot, s))
+        sc.sort()
+        row = [(s, -negv) for negv, s in sc[:k]]
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_exact_brute_force(seed):
+    rnd = random.Random(seed)
+    S, T, H, D = 11, 6, 3, 5
+    m = rnd.choice([1, 2, 3])
+    k = rnd.choice([1, 2, 4, 7])
+    q_pos0 = rnd.choice([0, 0, 3])
+    # small dyadic values: every product and sum is exact in float64, and ties happen
+    grid = [x / 2 for x in range(-6, 7)]
+    qv = [[[Fraction(rnd.choice(grid)) for _ in range(D)] for _ in range(H)] for _ in range(S)]
+    kv = [[Fraction(rnd.choice(grid)) for _ in range(D)] for _ in range(T)]
+    wv = [[Fraction(rnd.choice([-2, -1, -0.5, 0.5, 1, 1.5])) for _ in range(H)] for _ in range(S)]
+    q = torch.tensor([[[float(x) for x in row] for row in head] for head in qv])[None].to(torch.bfloat16)
+    kc = torch.tensor([[float(x) for x in row] for row in kv])[None].to(torch.bfloat16)
+    w = np.asarray([[float(x) for x in row] for row in wv], dtype=np.float32)[None]
+    idx, val = oracle.indexer_topk(bits(q), bits(kc), w, m, k, q_pos0=q_pos0)
+    ref = _brute_force(qv, kv, wv, m, k, q_pos0)
+    for t in range(S):
+        want_idx = [s for s, _ in ref[t]] + [-1] * (k - len(ref[t]))
+        want_val = [float(v) for _, v in ref[t]] + [-math.inf] * (k - len(ref[t]))
+        assert idx[0, t].tolist() == want_idx, (seed, t)
+        assert val[0, t].tolist() == want_val, (seed, t)
+
+
+def test_brute_force_with_bf16_rounded_values():
+    """Random normal values (rounded to bf16 first): scores within 1e-12 relative of
+    the exact rational result, and the same index sets wherever the gap between the
+    k-th and (k+1)-th exact score is not tiny."""
+    rnd = np.random.default_rng(7)
+    S, T, H, D, m, k = 9, 8, 4, 16, 1, 3
+    q = torch.from_numpy(rnd.standard_normal((1, S, H, D)).astype(np.float32)).to(torch.bfloat16)
+    kc = torch.from_numpy(rnd.standard_normal((1, T, D)).astype(np.float32)).to(torch.bfloat16)
+    w = rnd.standard_normal((1, S, H)).astype(np.float32)
+    qv = [[[Fraction(float(x)) for x in q[0, t, h].float()] for h in range(H)] for t in range(S)]
+    kv = [[Fraction(float(x)) for x in kc[0, s].float()] for s in range(T)]
+    wv = [[Fraction(float(x)) for x in w[0, t]] for t in range(S)]
+    idx, val = oracle.indexer_topk(bits(q), bits(kc), w, m, k)
+    ref = _brute_force(qv, kv, wv, m, k, 0)
+    for t in range(S):
+        for j, (s, v) in enumerate(ref[t]):
+            assert idx[0, t, j] == s
+            assert abs(val[0, t, j] - float(v)) <= 1e-12 * max(1.0, abs(float(v)))
+
+
+# ---------------------------------------------------------------------------
+# Special case that reduces to a library routine
+# ---------------------------------------------------------------------------
+
+def test_single_head_nonnegative_reduces_to_matmul_topk():
+    """H = 1, w = 1 and non-negative q, k: ReLU is the identity and the score matrix is
+    q @ k^T; torch.topk on the causally masked matrix gives the same selection."""
+    rnd = np.random.default_rng(3)
+    S, T, D, m, k = 64, 16, 128, 4, 5
+    q = torch.from_numpy(np.abs(rnd.standard_normal((1, S, 1, D))).astype(np.float32)).to(torch.bfloat16)
+    kc = torch.from_numpy(np.abs(rnd.standard_normal((1, T, D))).astype(np.float32)).to(torch.bfloat16)
+    w = np.ones((1, S, 1), dtype=np.float32)
+    idx, val = oracle.indexer_topk(bits(q), bits(kc), w, m, k)
+    full = q[0, :, 0].double() @ kc[0].double().T                    # [S, T]
+    t = torch.arange(S)[:, None]
+    s = torch.arange(T)[None, :]
+    full = full.masked_fill((s + 1) * m > t + 1, -math.inf)
+    ref_val, ref_idx = torch.topk(full, k, dim=1)
+    for r in range(S):
+        n = min(T, (r + 1) // m)
+        nk = min(k, n)
+        assert idx[0, r, :nk].tolist() == ref_idx[r, :nk].tolist()
+        np.testing.assert_allclose(val[0, r, :nk], ref_val[r, :nk].numpy(), rtol=1e-12)
+        assert (idx[0, r, nk:] == -1).all() and np.isneginf(val[0, r, nk:]).all()
+
+
+def test_large_k_is_full_stable_sort():
+    """k >= n_t returns every visible key, sorted by (score desc, index asc)."""
+    spec = synth.InputSpec(B=1, S=40, T=10, H=2, D=128, m=4, k=64, seed=11)
+    x = synth.make_inputs(spec)
+    idx, val = oracle.indexer_topk(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), 4, 64)
+    rows = oracle.score_rows(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), 4)
+    for t in range(spec.S):
+        n = oracle.visible_count(t, 4, spec.T)
+        order = sorted(range(n), key=lambda s: (-rows[t, s], s))
+        assert idx[0, t, :n].tolist() == order
+        assert (idx[0, t, n:] == -1).all()
+
+
+# ---------------------------------------------------------------------------
+# Number formats: exhaustive against torch's own casts
+# ---------------------------------------------------------------------------
+
+def test_bf16_decoder_exhaustive():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_bits_to_f64(allbits)
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3fn_decoder_exhaustive():
+    allbits = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3fn_bits_to_f64(allbits)
+    ref = torch.from_numpy(allbits).view(torch.float8_e4m3fn).double().numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+    finite = mine[np.isfinite(mine)]
+    assert np.nanmax(np.abs(finite)) == 448.0
+    assert int(np.isnan(mine).sum()) == 2                      # S.1111.111 only
+    # every finite E4M3 value is exact in bf16, so an exact up-conversion exists
+    as_bf16 = torch.from_numpy(finite.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert (as_bf16 == finite).all()
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def test_materialized_tensor_is_256_gib_at_64k():
+    """[B, S, H_I, T] fp32 at S = 65,536, H_I = 64, m = 4 (T = 16,384): 2^38 bytes, the
+    256 GB intermediate of the StreamIndex abstract."""
+    assert oracle.materialized_score_bytes(1, 65536, 64, 65536 // 4) == 2 ** 38
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "v4flash", "long"])
+def test_visible_pair_count_closed_form(name):
+    """With S = m T and m = 4: sum_t min(T, floor((t+1)/m)) = m T (T-1)/2 + T = T(2T-1)."""
+    spec = synth.CONFIGS[name]
+    T = spec.T
+    assert spec.S == spec.m * T
+    assert oracle.total_visible_pairs(spec.S, T, spec.m) == T * (2 * T - 1)
+
+
+def test_visible_count_boundaries():
+    for m in (1, 2, 3, 4, 7):
+        for t in range(40):
+            n = oracle.visible_count(t, m, 1000)
+            assert all((s + 1) * m <= t + 1 for s in range(n))
+            assert (n + 1) * m > t + 1
+    assert oracle.visible_count(10 ** 6, 4, 5) == 5
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def _small_inputs(seed=5, **kw):
+    spec = synth.InputSpec(B=2, S=96, T=24, H=4, D=128, m=4, k=8, seed=seed, **kw)
+    return spec, synth.make_inputs(spec)
+
+
+def test_weight_scaling_doubles_scores_exactly():
+    spec, x = _small_inputs()
+    i1, v1 = oracle.indexer_topk(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), 4, 8)
+    i2, v2 = oracle.indexer_topk(bits(x["q"]), bits(x["kc"]), 2 * x["w"].numpy(), 4, 8)
+    np.testing.assert_array_equal(i1, i2)
+    np.testing.assert_array_equal(2 * v1, v2)
+
+
+def test_rows_are_independent_and_offset_slices_agree():
+    spec, x = _small_inputs()
+    qb, kb, w = bits(x["q"]), bits(x["kc"]), x["w"].numpy()
+    full_i, full_v = oracle.indexer_topk(qb, kb, w, 4, 8)
+    sub_i, sub_v = oracle.indexer_topk(qb[:, 40:70], kb, w[:, 40:70], 4, 8, q_pos0=40)
+    np.testing.assert_array_equal(full_i[:, 40:70], sub_i)
+    np.testing.assert_array_equal(full_v[:, 40:70], sub_v)
+    one_i, one_v = oracle.indexer_topk(qb[1:], kb[1:], w[1:], 4, 8, rows=[77])
+    np.testing.assert_array_equal(full_i[1:, 77:78], one_i)
+
+
+def test_keys_past_visible_range_do_not_matter():
+    spec, x = _small_inputs()
+    qb, kb, w = bits(x["q"]), bits(x["kc"]).copy(), x["w"].numpy()
+    i1, v1 = oracle.indexer_topk(qb, kb, w, 4, 8, rows=range(0, 40))
+    kb[:, 10:] = 0x7F7F                                   # huge keys past row 39's view
+    i2, v2 = oracle.indexer_topk(qb, kb, w, 4, 8, rows=range(0, 40))
+    np.testing.assert_array_equal(i1, i2)
+    np.testing.assert_array_equal(v1, v2)
+
+
+def test_duplicate_keys_tie_exactly_and_lower_index_wins():
+    spec = synth.CONFIGS["small"].replace(S=2048, T=512, H=8, k=64)
+    x = synth.make_inputs(spec)
+    pairs = synth.duplicate_pairs(spec, 0)
+    assert pairs
+    rows = oracle.score_rows(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), 4, rows=[2047])
+    for s, src in pairs:
+        assert rows[0, s] == rows[0, src]
+    idx, _ = oracle.indexer_topk(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), 4, 64, rows=[2047])
+    pos = {int(s): j for j, s in enumerate(idx[0, 0]) if s >= 0}
+    for s, src in pairs:
+        if s in pos and src in pos:
+            assert pos[src] < pos[s]
+
+
+def test_fp32_evaluation_stays_inside_error_bound():
+    """A sequential float32 evaluation of the score (the same formula, ordinary
+    rounding) stays within the forward-error bound the oracle reports."""
+    spec, x = _small_inputs(seed=9)
+    qb, kb, w = bits(x["q"]), bits(x["kc"]), x["w"].numpy()
+    rows = list(range(30, 96))
+    exact = oracle.score_rows(qb, kb, w, 4, rows=rows)
+    bound = oracle.score_error_bound(qb, kb, w, 4, rows=rows)
+    qf = x["q"][0].float().numpy()
+    kf = x["kc"][0].float().numpy()
+    for i, t in enumerate(rows):
+        n = oracle.visible_count(t, 4, spec.T)
+        for s in range(n):
+            acc = np.float32(0)
+            for h in range(spec.H):
+                z = np.float32(0)
+                for d in range(spec.D):
+                    z = np.float32(z + np.float32(qf[t, h, d] * kf[s, d]))
+                acc = np.float32(acc + np.float32(w[0, t, h] * max(z, np.float32(0))))
+            assert abs(float(acc) - exact[i, s]) <= bound[i, s]
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: every one must be caught by a pin above
+# ---------------------------------------------------------------------------
+
+def _no_relu(q_row, w_row, keys, scale):
+    return w_row @ ((q_row @ keys.T) * scale[None, :])
+
+
+def _relu_after_weight(q_row, w_row, keys, scale):
+    return np.maximum(w_row[:, None] * ((q_row @ keys.T) * scale[None, :]), 0.0).sum(0)
+
+
+def _no_scale(q_row, w_row, keys, scale):
+    return w_row @ np.maximum(q_row @ keys.T, 0.0)
+
+
+def _mask_off_by_one(t_abs, m, T):
+    return max(0, min(T, (t_abs + 2) // m))
+
+
+def _higher_index_first(scores, k):
+    n = scores.shape[0]
+    order = np.lexsort((-np.arange(n), -scores))
+    keep = order[: min(k, n)]
+    idx = np.full(k, -1, dtype=np.int64)
+    val = np.full(k, -np.inf)
+    idx[: keep.shape[0]] = keep
+    val[: keep.shape[0]] = scores[keep]
+    return idx, val
+
+
+def _bad_bias_table():
+    t = OI.E4M3FN_TABLE.copy()
+    return t * 2.0
+
+
+@pytest.mark.parametrize("mutant", ["no_relu", "relu_after_weight", "no_scale",
+                                    "mask_off_by_one", "higher_index_first", "e4m3_bias"])
+def test_planted_mistakes_are_caught(mutant, monkeypatch):
+    if mutant == "no_relu":
+        monkeypatch.setattr(OI, "score_row", _no_relu)
+    elif mutant == "relu_after_weight":
+        monkeypatch.setattr(OI, "score_row", _relu_after_weight)
+    elif mutant == "no_scale":
+        monkeypatch.setattr(OI, "score_row", _no_scale)
+    elif mutant == "mask_off_by_one":
+        monkeypatch.setattr(OI, "visible_count", _mask_off_by_one)
+    elif mutant == "higher_index_first":
+        monkeypatch.setattr(OI, "select_topk", _higher_index_first)
+    elif mutant == "e4m3_bias":
+        monkeypatch.setattr(OI, "E4M3FN_TABLE", _bad_bias_table())
+    caught = 0
+    for case in CASES:
+        try:
+            _check_hand(case)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, mutant
