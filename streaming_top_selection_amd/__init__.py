@@ -1,0 +1,26 @@
+"""MI355X (gfx950) lightning-indexer top-k: streaming scoring + partition-merge top-k.
+
+The compute path is ``libsi_indexer.so`` (hand-written HIP kernels behind a C ABI,
+``include/si_indexer.h``); this package only marshals torch tensors into it.  Importing
+it loads the library and fails if it has not been built.
+"""
+
+from . import _lib
+from .api import (  # noqa: F401
+    Plan,
+    indexer_merge_chunk,
+    indexer_select_chunk,
+    indexer_topk,
+    materialize_scores,
+    materialize_topk,
+    plan,
+    workspace,
+)
+from ._lib import SiError  # noqa: F401
+
+_lib.load()
+
+__all__ = [
+    "Plan", "SiError", "indexer_topk", "indexer_select_chunk", "indexer_merge_chunk",
+    "materialize_scores", "materialize_topk", "plan", "workspace",
+]
