@@ -61,7 +61,7 @@ typedef enum si_dtype {
  * chunk size needs tuning per GPU: "Streamindex Csa Topk", Pitfalls). */
 typedef struct si_config {
     int32_t key_tile;       /* keys scored before the running top-k is updated:
-                               64, 128, 256, 512 (auto) or 1024                    */
+                               64, 128, 256, 512, 768 or 1024 (0 = auto)           */
     int32_t query_chunk;    /* query rows per driver step (bounds the workspace);
                                rounded up to a multiple of 32                       */
     int32_t key_partition;  /* keys per partition whose local top-k lists are merged;

@@ -178,11 +178,39 @@ struct LdsKeys {                      // keys buf[0..n) in LDS, strided over lan
 // wave.  Keys are unique, so the result is the exact rank-th key.  The result
 // is wave-uniform.  Requires 1 <= rank <= number of non-zero keys.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), off);
+        uint32_t hi = __shfl_xor((unsigned)(v >> 32), off);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
 template <class Src>
 __device__ uint64_t wave_select_kth(const Src& src, int rank, uint32_t* hist) {
     const int lane = lane_id();
-    uint64_t prefix = 0, pmask = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    // Leading bytes shared by every key (those where the smallest and the largest key
+    // agree) hold no information: start below them.  Candidates above a threshold
+    // usually share their top score bytes, which would otherwise send every key to one
+    // histogram bin.
+    uint64_t lo = ~0ull, hi = 0ull;
+    src.for_each([&](uint64_t v) {
+        if (v != 0ull) {
+            lo = v < lo ? v : lo;
+            hi = v > hi ? v : hi;
+        }
+    });
+    lo = wave_min_u64(lo);
+    hi = wave_max_u64(hi);
+    const uint64_t diff = lo ^ hi;
+    if (diff == 0ull) return lo;              // a single distinct key
+    const int top = 63 - __clzll((long long)diff);   // highest differing bit
+    int shift = (top / 8) * 8;
+    uint64_t pmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+    uint64_t prefix = lo & pmask;
+    for (; shift >= 0; shift -= 8) {
         for (int i = lane; i < 256; i += 64) hist[i] = 0u;
         wave_sync();
         src.for_each([&](uint64_t v) {

@@ -13,6 +13,7 @@ template <bool FP8>
 __global__ void __launch_bounds__(512) mat_score_kernel(MatScoreArgs A) {
     constexpr int NWAVE = 8, KB = 2, RT = NWAVE * KB * kMB;
     __shared__ ScoreLds L;
+    SI_DECLARE_QBUFS(Q);
     const Problem& P = A.P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -31,7 +32,7 @@ __global__ void __launch_bounds__(512) mat_score_kernel(MatScoreArgs A) {
     if (live) {
         load_w_tile<NWAVE * 64>(P, b, trow0, rows_valid, L);
         __syncthreads();
-        score_regs<NWAVE, KB, FP8>(P, b, trow0, rows_valid, key0, L, acc);
+        score_regs<NWAVE, KB, FP8>(P, b, trow0, rows_valid, key0, L, Q, acc);
     }
     const int qj = lane & 31;
     const int64_t row = trow0 + qj;

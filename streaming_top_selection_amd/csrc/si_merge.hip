@@ -26,7 +26,9 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeArgs A) {
     const int64_t slot0 = (b * A.QC + r) * A.P_ws;
 
     // gather the partition lists
-    const int c = lane < Pt ? A.cnt[slot0 + lane] : 0;
+    // each list holds at most k keys; the clamp keeps a corrupted count from driving
+    // the loops below past the LDS buffer
+    const int c = lane < Pt ? min(max(A.cnt[slot0 + lane], 0), A.k) : 0;
     const int off = wave_excl_scan(c);
     const int total = wave_sum(c);
     for (int p = 0; p < Pt; ++p) {

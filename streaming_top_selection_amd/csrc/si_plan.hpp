@@ -74,13 +74,14 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
         case 128:  pl.nwave = 4; pl.kb = 1; pl.nsub = 1; break;
         case 256:  pl.nwave = 8; pl.kb = 1; pl.nsub = 1; break;
         case 512:  pl.nwave = 8; pl.kb = 2; pl.nsub = 1; break;
+        case 768:  pl.nwave = 4; pl.kb = 6; pl.nsub = 1; break;
         case 1024: pl.nwave = 8; pl.kb = 2; pl.nsub = 2; break;
         default:
-            msg = "key_tile must be 64, 128, 256, 512 or 1024"; return SI_ERR_UNSUPPORTED;
+            msg = "key_tile must be 64, 128, 256, 512, 768 or 1024"; return SI_ERR_UNSUPPORTED;
     }
-    // candidate slots per (query, partition): room for k kept keys plus at least one
-    // key tile of arrivals, and at least 2k so a compaction frees half the buffer
-    const int32_t cg = (kt <= 512 && k <= 1024) ? 2048 : 4096;
+    // candidate slots per (query, partition): room for k kept keys plus a key tile of
+    // arrivals with slack, and at least 2k so a compaction frees half the buffer
+    const int32_t cg = (2 * k <= 2048 && k + kt + 256 <= 2048) ? 2048 : 4096;
 
     const int64_t t_eff = (S == 0) ? 0 : visible_count_host(q_pos0 + S - 1, m, T);
     const int64_t q_tiles = B * ceil_div(S, kPlanTQ);

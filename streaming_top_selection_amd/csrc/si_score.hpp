@@ -11,11 +11,16 @@
 // Data flow (MI355X layout, not the pages' Triton design):
 //  * K-stationary: each wave loads its keys once into MFMA A-operand registers and
 //    keeps them for all heads (a key tile is the same for every head).
-//  * q is streamed head by head through a double-buffered LDS tile of 32 rows x 128
-//    bf16 (8 KiB/head) that all waves of the workgroup share as the B operand.
+//  * q is streamed head by head into LDS tiles of 32 rows x 128 bf16 (8 KiB/head) by
+//    direct global->LDS loads issued several heads ahead (no register staging);
+//    all waves of the workgroup share each tile as the MFMA B operand.
+//  * Software pipeline: the MFMAs of head h+1 are issued interleaved with the VALU
+//    epilogue (ReLU, weighted sum) of head h, so both pipes stay busy in each wave.
 //  * Output layout: lane l owns query column (l & 31) and key rows mfma_row(r, l),
 //    so the head weight w[t,h] is one LDS read per lane per head.
 #pragma once
+
+#include <type_traits>
 
 #include "si_common.hpp"
 
@@ -31,23 +36,54 @@ struct Problem {
     int64_t q_pos0;
 };
 
-constexpr int kQRow = kD + 8;     // staged q row in bf16 (272 bytes: bank-skewed rows)
-constexpr int kWStride = kMaxH + 1;  // w row stride in floats (odd: conflict-free column reads)
+constexpr int kQBuf = 8;             // q tiles in flight: head h+7 loads while h+1 is read
+constexpr int kWStride = kMaxH + kQBuf + 1;  // w row: H weights, zero pad, odd stride
+constexpr int kQRowSlots = 17;       // 16-byte slots per staged q row: 16 data + 1 pad
+constexpr int kQRow = kQRowSlots * 8;        // staged q row in bf16 (272 bytes)
+constexpr int kQSlots = kTQ * kQRowSlots;    // 16-byte slots per staged q tile
+constexpr int kQTile = kTQ * kQRow;          // bf16 per staged q tile
 
 struct ScoreLds {
-    uint16_t q[2][kTQ * kQRow];   // double-buffered q tile of one head
-    float w[kTQ * kWStride];      // head weights of the 32 query rows
+    float w[kTQ * kWStride];      // head weights of the 32 query rows (0 past H)
 };
+
+// The staged q tiles: kQBuf separate LDS arrays (each its own object, so the
+// compiler can tell the direct-to-LDS loads into one from reads of another).  Row j
+// of a tile starts at 16-byte slot 17*j, so the B-operand reads (16 rows at a time,
+// the same 16-byte piece of each) hit 16 different bank groups.
+struct QBufs {
+    uint16_t* p[kQBuf];
+};
+
+#define SI_DECLARE_QBUFS(name)                                                        \
+    __shared__ __attribute__((aligned(16))) uint16_t name##0[si::kQTile],            \
+        name##1[si::kQTile], name##2[si::kQTile], name##3[si::kQTile],               \
+        name##4[si::kQTile], name##5[si::kQTile], name##6[si::kQTile],               \
+        name##7[si::kQTile];                                                          \
+    const si::QBufs name = {{name##0, name##1, name##2, name##3, name##4, name##5,   \
+                             name##6, name##7}}
+
+// Workgroup barrier for the head loop.  LDS visibility is managed explicitly: the
+// direct-to-LDS loads are awaited with vmcnt before it and every LDS read feeding an
+// MFMA is awaited before its use, so only the compiler must not move memory accesses
+// across it (a release fence here would wait for every load in flight).
+__device__ __forceinline__ void loop_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding).
+#define SI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | 0x70 | 0xF00)
 
 // Fills L.w for query rows [row0, row0 + rows_valid) of batch entry b (0 past the end).
 template <int NT>
 __device__ __forceinline__ void load_w_tile(const Problem& P, int64_t b, int64_t row0,
                                             int rows_valid, ScoreLds& L) {
     const int H = P.H;
-    for (int f = threadIdx.x; f < kTQ * H; f += NT) {
-        const int j = f / H, h = f - j * H;
-        L.w[j * kWStride + h] =
-            j < rows_valid ? P.w[((b * P.S + row0 + j) * H) + h] : 0.0f;
+    for (int f = threadIdx.x; f < kTQ * kWStride; f += NT) {
+        const int j = f / kWStride, h = f - j * kWStride;
+        L.w[f] = (j < rows_valid && h < H) ? P.w[((b * P.S + row0 + j) * H) + h] : 0.0f;
     }
 }
 
@@ -58,11 +94,9 @@ __device__ __forceinline__ void load_w_tile(const Problem& P, int64_t b, int64_t
 template <int NWAVE, int KB, bool FP8>
 __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t row0,
                                            int rows_valid, int64_t key0, ScoreLds& L,
-                                           f32x16 (&acc)[KB]) {
+                                           const QBufs& Q, f32x16 (&acc)[KB]) {
     constexpr int NT = NWAVE * kWave;
-    constexpr int QCHUNKS = kTQ * (kD * 2 / 16);   // 16-byte pieces of one head tile
-    constexpr int QPER = QCHUNKS / NT;
-    static_assert(QCHUNKS % NT == 0, "q tile must split evenly over the workgroup");
+    static_assert(kQBuf >= 4, "the pipeline reads head h+1 while loading h+kQBuf-1");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -104,27 +138,64 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
         }
     }
 
-    // ---- q staging: 16-byte pieces, row j = f / 16, piece c = f % 16 -----------
-    u32x4 qreg[QPER];
-    auto qload = [&](int h) {
+    // ---- q staging: direct global -> LDS loads, kQBuf - 2 heads ahead ----------
+    // Slot t of a head's tile (row t / 17, piece t % 17; piece 16 is the row pad and
+    // receives a copy of piece 15) is filled by thread t mod NT in round t / NT; each
+    // wave instruction writes 64 consecutive slots, as the LDS-DMA load requires.
+    // Rows past the tile's end re-load the last valid row (weights 0, never selected)
+    // and heads past H-1 re-load head H-1, so every step issues the same loads.
+    constexpr int QPER = (kQSlots + NT - 1) / NT;
+    // loads per head issued by the wave with the fewest (the last one)
+    constexpr int QMIN = ((kQSlots - (NWAVE - 1) * 64) + NT - 1) / NT;
+    constexpr int AHEAD = kQBuf - 2;
+    int64_t qoff[QPER];
+#pragma unroll
+    for (int n = 0; n < QPER; ++n) {
+        const int slot = tid + n * NT;
+        const int jr = slot / kQRowSlots;
+        const int c = min(slot - jr * kQRowSlots, 15);
+        const int j = min(jr, rows_valid - 1);
+        qoff[n] = ((b * P.S + row0 + j) * H) * (int64_t)kD + c * 8;
+    }
+    auto qload = [&](uint16_t* buf, int h) {
+        const int64_t hc = h < H ? h : H - 1;
 #pragma unroll
         for (int n = 0; n < QPER; ++n) {
-            const int f = tid + n * NT;
-            const int j = f >> 4, c = f & 15;
-            if (j < rows_valid) {
-                qreg[n] = *reinterpret_cast<const u32x4*>(
-                    P.q + (((b * P.S + row0 + j) * H + h) * kD + c * 8));
-            } else {
-                qreg[n] = u32x4{0u, 0u, 0u, 0u};
+            const int base = wave * 64 + n * NT;          // first slot of this wave's row
+            if (base < kQSlots && base + lane < kQSlots) {
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)(P.q + qoff[n] + hc * kD),
+                    (__attribute__((address_space(3))) void*)(buf + base * 8), 16, 0, 0);
             }
         }
     };
-    auto qstore = [&](int buf) {
+    auto qread = [&](const uint16_t* buf, bf16x8 (&bq)[8]) {
+        const uint16_t* row = buf + il * kQRow + 64 * hh;
 #pragma unroll
-        for (int n = 0; n < QPER; ++n) {
-            const int f = tid + n * NT;
-            const int j = f >> 4, c = f & 15;
-            *reinterpret_cast<u32x4*>(&L.q[buf][j * kQRow + c * 8]) = qreg[n];
+        for (int s = 0; s < 8; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
+    };
+    // MFMA chain of key block kb for one head: z = A(kb) * B over d, from zero
+    auto mfma_block = [&](int kb, const bf16x8 (&bq)[8], f32x16& z) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) z = mfma32x32x16(kf[kb][s], bq[s], z);
+    };
+    auto epilogue_block = [&](int kb, const f32x16& z, float wh) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[kb][r] = __builtin_fmaf(wh, __builtin_fmaxf(z[r], 0.0f), acc[kb][r]);
+    };
+    // Keeps an accumulator block's epilogue inside the step that issues it (without
+    // this the compiler sinks every epilogue of the unrolled loop to its end and keeps
+    // all their MFMA outputs alive at once).
+    auto pin = [&](f32x16& v) { asm volatile("" : "+v"(v)); };
+    // one MFMA block (8 MFMAs) interleaved with one epilogue block (32 VALU)
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
         }
     };
 
@@ -133,38 +204,84 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[kb][r] = 0.0f;
 
-    qload(0);
-    qstore(0);
-    __syncthreads();
-
-    for (int h = 0; h < H; ++h) {
-        const int buf = h & 1;
-        if (h + 1 < H) qload(h + 1);
-
-        bf16x8 bq[8];
-        const uint16_t* qrow = &L.q[buf][il * kQRow + 64 * hh];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
-
-        f32x16 z[KB];
+    // Skewed software pipeline over blocks (head, key block), in the order
+    // (0,0), (0,1), ..., (0,KB-1), (1,0), ...: the MFMA chain of block X + ZR - 1 is
+    // issued interleaved with the epilogue (ReLU, weighted sum) of block X, so an
+    // epilogue never waits on a chain that was just issued, and block X lives in
+    // accumulator slot X mod ZR.  The B operand of head h+1 (bq[(h+1) % 2]) is read at
+    // the start of step h, ahead of its first use.
+    //
+    // Step h (buffers known at compile time): read head h+1 from buffer (h+1) % 8;
+    // for kb = 0..KB-1 run the MFMAs of block (h, kb) + ZR - 1 beside the epilogue of
+    // (h, kb); load head h+7 into buffer (h+7) % 8 (last read in step h-1); publish
+    // head h+2.  Heads run in groups of 8; steps past H-1 see zero head weights (their
+    // epilogue adds exact zeros) and re-loaded data of head H-1, so the arithmetic of
+    // every real head is the same for any H.
+    constexpr int ZR = (KB == 1) ? 2 : ((KB % 3 == 0) ? 3 : 2);   // accumulator slots
+    constexpr int LA = ZR - 1;                                     // blocks of lookahead
+    static_assert((kQBuf * KB) % ZR == 0, "slots must repeat every group of 8 heads");
+    static_assert(LA <= KB, "lookahead stays within the next head");
+    f32x16 z[ZR];
+    bf16x8 bq[2][8];
+    auto step = [&](auto rstep, int h) {
+        constexpr int R = decltype(rstep)::value;            // h mod 8
+        constexpr int RB = (R + 1) % kQBuf, LB = (R + kQBuf - 1) % kQBuf;
+        constexpr int C = R % 2, N = 1 - C;
+        const float wh = L.w[il * kWStride + h];
+        qread(Q.p[RB], bq[N]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z[kb][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) z[kb] = mfma32x32x16(kf[kb][s], bq[s], z[kb]);
+            const int x = R * KB + kb;                        // block index mod 8*KB
+            const int ykb = (kb + LA) % KB;                   // block x + LA
+            const bool next_head = kb + LA >= KB;
+            mfma_block(ykb, next_head ? bq[N] : bq[C], z[(x + LA) % ZR]);
+            epilogue_block(kb, z[x % ZR], wh);
+            interleave();
+            pin(acc[kb]);
         }
+        qload(Q.p[LB], h + AHEAD + 1);
+        // head h+2 (read in step h+1) must have landed: every wave issues at least
+        // QMIN loads per head, so <= (AHEAD-1)*QMIN younger loads means it has
+        SI_WAIT_VMCNT((AHEAD - 1) * QMIN);
+        loop_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    static_assert(kQBuf == 8 && AHEAD == 6, "the unrolled loop below assumes 8 buffers");
 
-        const float wh = L.w[il * kWStride + h];
+    // prologue: heads 0..6 in flight into buffers 0..6, heads 0 and 1 published
+    qload(Q.p[0], 0);
+    qload(Q.p[1], 1);
+    qload(Q.p[2], 2);
+    qload(Q.p[3], 3);
+    qload(Q.p[4], 4);
+    qload(Q.p[5], 5);
+    qload(Q.p[6], 6);
+    SI_WAIT_VMCNT((AHEAD - 1) * QMIN);
+    loop_barrier();
+    qread(Q.p[0], bq[0]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[kb][r] = __builtin_fmaf(wh, __builtin_fmaxf(z[kb][r], 0.0f), acc[kb][r]);
+    for (int x = 0; x < LA; ++x) mfma_block(x, bq[0], z[x]);   // blocks (0, 0..LA-1)
 
-        if (h + 1 < H) qstore(buf ^ 1);
-        __syncthreads();
+    for (int h = 0; h < H; h += kQBuf) {
+        step(I0{}, h + 0);
+        step(I1{}, h + 1);
+        step(I2{}, h + 2);
+        step(I3{}, h + 3);
+        step(I4{}, h + 4);
+        step(I5{}, h + 5);
+        step(I6{}, h + 6);
+        step(I7{}, h + 7);
     }
+
+    // the last steps' loads (of padding heads) land before anything else uses LDS
+    SI_WAIT_VMCNT(0);
 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {

@@ -26,6 +26,30 @@
 
 namespace si {
 
+// Reduces one query's candidate buffer buf[0, cnt) (cnt > k, unique keys) to its exact
+// top k, in place, and returns the k-th key.  Called by a whole wave; kept out of
+// line so its E keys per lane do not add to the scoring loop's register budget.
+template <int E>
+__device__ __noinline__ uint64_t compact_to_topk(uint64_t* buf, int cnt, int k,
+                                                 uint32_t* hist) {
+    const int lane = lane_id();
+    RegKeys<E> R;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = e * 64 + lane;
+        R.v[e] = i < cnt ? buf[i] : 0ull;
+    }
+    const uint64_t kth = wave_select_kth(R, k, hist);
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) mine += (R.v[e] >= kth) ? 1 : 0;
+    uint64_t* dst = buf + wave_excl_scan(mine);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (R.v[e] >= kth) *dst++ = R.v[e];
+    return kth;
+}
+
 template <int NWAVE, int KB, int NSUB, int CG, bool FP8>
 __global__ void __launch_bounds__(NWAVE * 64)
 select_kernel(SelectArgs A) {
@@ -36,6 +60,7 @@ select_kernel(SelectArgs A) {
     static_assert(CG % 64 == 0, "capacity must be a multiple of the wave size");
 
     __shared__ ScoreLds L;
+    SI_DECLARE_QBUFS(Q);
     __shared__ uint64_t sTheta[kTQ];
     __shared__ int32_t sCnt[kTQ];
     __shared__ int32_t sN[kTQ];
@@ -81,30 +106,48 @@ select_kernel(SelectArgs A) {
     int sub = 0;
     for (int64_t key0 = key_lo; key0 < key_hi; key0 += RT) {
         f32x16 acc[KB];
-        score_regs<NWAVE, KB, FP8>(P, b, row0, rows_valid, key0, L, acc);
+        score_regs<NWAVE, KB, FP8>(P, b, row0, rows_valid, key0, L, Q, acc);
 
         // ---- filter against the running threshold, append survivors ----------
+        // A key beats theta iff its score is larger than theta's score, or equal with
+        // a lower index; the float compare decides almost every case in one op.  The
+        // causal mask only needs checking when the tile crosses this query's end.
         const int nj = sN[qj];
         const uint64_t th = sTheta[qj];
+        const float thf = th == 0ull ? -__builtin_inff() : key_score(th);
+        const uint32_t th_lo = (uint32_t)th;
         const int64_t kbase = key0 + (int64_t)wave * KB * kMB;
-        int c = 0;
+        const bool full = kbase + KB * kMB <= nj;
+        uint32_t pass_bits[KB];                        // bit r of block kb: key passes
+        int npass = 0;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            uint32_t bits = 0;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                const float v = acc[kb][r];
                 const int64_t s = kbase + kb * kMB + mfma_row(r, lane);
-                c += (s < nj && make_key(acc[kb][r], (uint32_t)s) > th) ? 1 : 0;
+                bool pass = v > thf || (v == thf && th != 0ull && ~(uint32_t)s > th_lo);
+                if (!full) pass = pass && s < nj;
+                bits |= (pass ? 1u : 0u) << r;
             }
-        if (c) {
-            const int base = atomicAdd(&sCnt[qj], c);
-            uint64_t* dst = my_cand + base;
+            pass_bits[kb] = bits;
+            npass += __popc(bits);
+        }
+        if (npass) {
+            const int base = atomicAdd(&sCnt[qj], npass);
+            // the compaction policy keeps base + npass <= CG; the bound below only
+            // keeps a broken invariant from writing outside this query's buffer
+            int pos = base;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t s = kbase + kb * kMB + mfma_row(r, lane);
-                    const uint64_t key = make_key(acc[kb][r], (uint32_t)s);
-                    if (s < nj && key > th) *dst++ = key;
+                    if (pass_bits[kb] & (1u << r)) {
+                        const int64_t s = kbase + kb * kMB + mfma_row(r, lane);
+                        if (pos < CG) my_cand[pos] = make_key(acc[kb][r], (uint32_t)s);
+                        ++pos;
+                    }
                 }
         }
 
@@ -116,23 +159,10 @@ select_kernel(SelectArgs A) {
             __syncthreads();
             const int limit = last ? A.k : CG - KT;
             for (int jj = wave; jj < rows_valid; jj += NWAVE) {
-                const int cj = sCnt[jj];
+                const int cj = min(sCnt[jj], CG);
                 if (cj > limit) {
                     uint64_t* buf = A.cand + (slot0 + (int64_t)jj * A.P_ws) * CG;
-                    RegKeys<E> R;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int i = e * 64 + lane;
-                        R.v[e] = i < cj ? buf[i] : 0ull;
-                    }
-                    const uint64_t kth = wave_select_kth(R, A.k, sHist[wave]);
-                    int mine = 0;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) mine += (R.v[e] >= kth) ? 1 : 0;
-                    uint64_t* dst = buf + wave_excl_scan(mine);
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if (R.v[e] >= kth) *dst++ = R.v[e];
+                    const uint64_t kth = compact_to_topk<E>(buf, cj, A.k, sHist[wave]);
                     if (lane == 0) {
                         sCnt[jj] = A.k;
                         sTheta[jj] = kth;
@@ -142,7 +172,7 @@ select_kernel(SelectArgs A) {
             __syncthreads();
         }
     }
-    if (tid < rows_valid) A.cnt[slot0 + (int64_t)tid * A.P_ws] = sCnt[tid];
+    if (tid < rows_valid) A.cnt[slot0 + (int64_t)tid * A.P_ws] = min(sCnt[tid], A.k);
 }
 
 template <int NWAVE, int KB, int NSUB, int CG, bool FP8>
@@ -162,6 +192,7 @@ static hipError_t launch_tile(const SelectArgs& a, int nwave, int kb, int nsub,
     if (nwave == 8 && kb == 1 && nsub == 1) return launch_one<8, 1, 1, CG, FP8>(a, stream);
     if (nwave == 8 && kb == 2 && nsub == 1) return launch_one<8, 2, 1, CG, FP8>(a, stream);
     if (nwave == 8 && kb == 2 && nsub == 2) return launch_one<8, 2, 2, CG, FP8>(a, stream);
+    if (nwave == 4 && kb == 6 && nsub == 1) return launch_one<4, 6, 1, CG, FP8>(a, stream);
     return hipErrorInvalidValue;
 }
 

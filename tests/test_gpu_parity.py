@@ -155,7 +155,7 @@ def test_knobs_bit_identical(gpu_lib):
     say("knobs")
     xd = dev(synth.make_inputs(spec))
     ref = run_mat(gpu_lib, xd, spec.m, spec.k)
-    for kt in (64, 128, 256, 512, 1024):
+    for kt in (64, 128, 256, 512, 768, 1024):
         for qc in (0, 96, 512):
             for kp in (0, kt if kt >= 128 else 128):
                 out = run_stream(gpu_lib, xd, spec.m, spec.k, key_tile=kt, query_chunk=qc,
@@ -227,7 +227,7 @@ def test_small_duplicates_chunk_sweep(gpu_lib):
     oa = oracle_args(xc, spec)
     ref = run_mat(gpu_lib, xd, spec.m, spec.k)
     for qc in (256, 512, 1024, 2048, 4096):
-        for kt in (64, 512, 1024):
+        for kt in (64, 512, 768, 1024):
             out = run_stream(gpu_lib, xd, spec.m, spec.k, query_chunk=qc, key_tile=kt)
             assert_same(out, ref, f"small query_chunk={qc} key_tile={kt}")
     # ties: each duplicated key scores exactly like its source, the lower index first
