@@ -58,6 +58,7 @@ def _shapes(q, kc, w, kc_scale):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kc {tuple(kc.shape)}, w {tuple(w.shape)}")
     if q.dtype != torch.bfloat16 or w.dtype != torch.float32:
         raise TypeError("q must be bfloat16 and w float32")
+    _kc_dtype(kc)
     for name, t in (("q", q), ("kc", kc), ("w", w), ("kc_scale", kc_scale)):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous GPU tensor")
