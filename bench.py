@@ -20,8 +20,11 @@ region.  Prints one JSON line:
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,6 +40,37 @@ WORKLOADS = {
     "small": "Small exactness check: B=2, S=8192, m=4, T=2048, H_I=64, D=128, top-k=512, 5% duplicate keys",
     "long": "Long-context: B=1, S=262144, m=4, T=65536, H_I=64, D=128, top-k=512",
 }
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["si_select.hip", "si_score.hpp", "si_common.hpp"]
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_v4flash_s65536.md")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    """SHA-256 (first 16 hex digits) of the fused select kernel's sources."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "streaming_top_selection_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per select launch from the committed counter summary, if it was taken
+    on the current kernel sources (else None: the counters no longer apply)."""
+    try:
+        text = open(PROFILE_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", text)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
 
 
 def visible_pairs(S, T, m, q_pos0=0):
@@ -103,7 +137,14 @@ def main(argv=None):
     ap.add_argument("--key-partition", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="bench", choices=["bench", "select-once", "copy-probe",
+                                                         "summarize"],
+                    help="select-once / copy-probe: single launches for rocprofv3 counter "
+                         "runs; summarize DIR: turn rocprofv3 CSV output into the summary")
+    ap.add_argument("--dir", default=None, help="rocprofv3 output root for --mode summarize")
     args = ap.parse_args(argv)
+    if args.mode == "summarize":
+        return summarize(args.dir)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -143,6 +184,23 @@ def main(argv=None):
                                    ws, out, kc_dtype=kc_dtype, **knobs)
             if events is not None:
                 events[c][2].record(stream)
+
+    if args.mode == "select-once":
+        step()
+        torch.cuda.synchronize(dev)
+        si.indexer_select_chunk(x["q"], x["kc"], x["w"], spec.m, spec.k, 0, ws,
+                                kc_scale=x["kc_scale"], **knobs)
+        torch.cuda.synchronize(dev)
+        print("select-once done", flush=True)
+        return 0
+    if args.mode == "copy-probe":
+        a = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize(dev)
+        b.copy_(a)
+        torch.cuda.synchronize(dev)
+        print(f"copy-probe done: {COPY_PROBE_BYTES} bytes read and written", flush=True)
+        return 0
 
     # the staged step is the product call: check once against si_indexer_topk itself
     step()
@@ -187,6 +245,8 @@ def main(argv=None):
     merge_bytes = kept * 8 + spec.B * spec.S * pl.n_partitions * 4 + spec.B * spec.S * spec.k * 8
     merge_gbps = merge_bytes / mrg_step_s / 1e9
 
+    traffic = committed_traffic() if args.workload == "v4flash" and not any(knobs.values()) \
+        else None
     rec = {
         "metric": METRIC,
         "value": pairs / step_s,
@@ -219,7 +279,7 @@ def main(argv=None):
             "peak": BF16_DENSE_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / BF16_DENSE_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "mean_launch_ms": sel_mean_s * 1e3,
             "launches_per_step": pl.n_chunks,
             "flops_per_step": flops,
@@ -240,6 +300,61 @@ def main(argv=None):
                                        "mean": float(np.mean(hits)) if hits else None,
                                        "min": float(np.min(hits)) if hits else None}
     print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _pmc_value(csv_dir, counter, kernel_substr):
+    """Counter value of the last dispatch whose kernel name contains kernel_substr."""
+    import csv
+    best = None
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if counter == r["Counter_Name"] and kernel_substr in r["Kernel_Name"]:
+                    d = int(r["Dispatch_Id"])
+                    if best is None or d > best[0]:
+                        best = (d, 0.0)
+                    if d == best[0]:
+                        best = (d, best[1] + float(r["Counter_Value"]))
+    return None if best is None else best[1]
+
+
+def _kernel_stats(csv_dir):
+    import csv
+    rows = []
+    for path in glob.glob(os.path.join(csv_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def summarize(root):
+    """Prints the markdown summary of a profile directory with subdirectories trace/
+    (kernel trace + stats), fetch/ and write/ (select-once counters) and copy_fetch/,
+    copy_write/ (copy-probe counters)."""
+    stats = _kernel_stats(os.path.join(root, "trace"))
+    sel = _pmc_value(os.path.join(root, "fetch"), "FETCH_SIZE", "select_kernel")
+    wr = _pmc_value(os.path.join(root, "write"), "WRITE_SIZE", "select_kernel")
+    cf = _pmc_value(os.path.join(root, "copy_fetch"), "FETCH_SIZE", "")
+    cw = _pmc_value(os.path.join(root, "copy_write"), "WRITE_SIZE", "")
+    fetch_scale = COPY_PROBE_BYTES / (cf * 1024) if cf else None
+    write_scale = COPY_PROBE_BYTES / (cw * 1024) if cw else None
+    fetch_b = sel * 1024 * fetch_scale if sel and fetch_scale else None
+    write_b = wr * 1024 * write_scale if wr and write_scale else None
+    print("| kernel | calls | total ms | average us | percent |")
+    print("|---|---|---|---|---|")
+    for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+        print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['TotalDurationNs'])/1e6:.3f} | "
+              f"{float(r['AverageNs'])/1e3:.1f} | {float(r['Percentage']):.2f} |")
+    print()
+    print(f"select_kernel FETCH_SIZE {sel} KiB, WRITE_SIZE {wr} KiB per launch")
+    print(f"copy probe ({COPY_PROBE_BYTES} B read + written): FETCH_SIZE {cf} KiB, "
+          f"WRITE_SIZE {cw} KiB -> scale fetch x{fetch_scale}, write x{write_scale}")
+    if fetch_b is not None and write_b is not None:
+        rec = {"kernel_source_sha256_16": kernel_source_hash(),
+               "fetch_bytes": fetch_b, "write_bytes": write_b,
+               "bytes_per_launch": fetch_b + write_b}
+        print(f"<!-- traffic {json.dumps(rec)} -->")
     return 0
 
 
