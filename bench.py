@@ -43,7 +43,8 @@ WORKLOADS = {
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["si_select.hip", "si_score.hpp", "si_common.hpp"]
+KERNEL_SOURCES = ["si_select.hpp", "si_select_kt512_bf16.hip", "si_compact.hpp", "si_score.hpp",
+                  "si_common.hpp"]
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_v4flash_s65536.md")
 COPY_PROBE_BYTES = 1 << 30
 

@@ -33,6 +33,9 @@ HIPCC_FLAGS = [
     "-fno-honor-nans",
     # packed fp32 VALU ops stay off: every fp32 op is an ordinary v_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results and accumulators in VGPRs: the epilogue reads every MFMA result
+    # with VALU ops, which cannot read AGPRs (the AGPRs then hold the key operands)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     f"-I{INCLUDE}",
@@ -57,7 +60,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    # the largest units (the KB = 4 select kernels) first, so the pool stays busy
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")),
+                     key=lambda f: (not ("kt512" in f or "kt1024" in f), f))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"

@@ -61,10 +61,8 @@ __device__ __forceinline__ float key_score(uint64_t key) {
     return unord_f32((uint32_t)(key >> 32));
 }
 
-// -0 -> +0, everything else unchanged.
-__device__ __forceinline__ float canon_zero(float x) {
-    return (__float_as_uint(x) == 0x80000000u) ? 0.0f : x;
-}
+// -0 -> +0, everything else unchanged (IEEE: -0 + +0 = +0, x + 0 = x for x != 0).
+__device__ __forceinline__ float canon_zero(float x) { return x + 0.0f; }
 
 // ---------------------------------------------------------------------------
 // OCP FP8 E4M3 byte -> bf16 bits.  Exact: every finite E4M3 value (3 mantissa
@@ -95,9 +93,17 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------
-// Wavefront primitives (64 lanes).
+// Wavefront primitives (64 lanes).  Reductions and scans move data between lanes
+// with DPP (a VALU operand modifier, no LDS round trip): butterflies within each
+// row of 16 lanes, then the four row results are combined with readlane or, for
+// scans, with the gfx9 row broadcasts.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+// the workgroup's wave index as a wave-uniform (scalar) value
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 
 // Orders this wave's LDS accesses before/after the call (LDS operations of one
 // wave are performed in issue order; this stops the compiler moving them).
@@ -107,36 +113,86 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-    uint32_t lo = __shfl((unsigned)(v & 0xFFFFFFFFu), src);
-    uint32_t hi = __shfl((unsigned)(v >> 32), src);
-    return ((uint64_t)hi << 32) | lo;
+// Workgroup barrier that waits for this wave's LDS operations only (global stores
+// may still be in flight): for publishing LDS counters between waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt unchanged
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowShr = 0x110;        // + n: row_shr:n
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// v from another lane by DPP; lanes the control does not write (row mask, or a
+// source outside the row) receive `old`
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    return ((uint64_t)readlane((uint32_t)(v >> 32), l) << 32) | readlane((uint32_t)v, l);
+}
+
+// butterfly step within rows of 16 lanes for a 64-bit value
+template <int CTRL, class Op>
+__device__ __forceinline__ uint64_t dpp_step64(uint64_t v, Op op) {
+    const uint32_t lo = dpp<CTRL>(0u, (uint32_t)v), hi = dpp<CTRL>(0u, (uint32_t)(v >> 32));
+    return op(v, ((uint64_t)hi << 32) | lo);
+}
+
+template <class Op>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t v, Op op) {
+    v = dpp_step64<kDppQuadSwap1>(v, op);
+    v = dpp_step64<kDppQuadSwap2>(v, op);
+    v = dpp_step64<kDppRowHalfMirror>(v, op);
+    v = dpp_step64<kDppRowMirror>(v, op);      // every lane holds its row's result
+    const uint64_t r0 = readlane64(v, 0), r1 = readlane64(v, 16);
+    const uint64_t r2 = readlane64(v, 32), r3 = readlane64(v, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+
+// wave-uniform max / min of a 64-bit value over the 64 lanes
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), off);
-        uint32_t hi = __shfl_xor((unsigned)(v >> 32), off);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
+}
+
+// inclusive prefix sum over lanes 0..lane
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    uint32_t x = v;
+    x += dpp<kDppRowShr + 1>(0u, x);
+    x += dpp<kDppRowShr + 2>(0u, x);
+    x += dpp<kDppRowShr + 4>(0u, x);
+    x += dpp<kDppRowShr + 8>(0u, x);           // scans within rows of 16
+    x += dpp<kDppRowBcast15, 0xA>(0u, x);      // rows 1, 3 add the row before
+    x += dpp<kDppRowBcast31, 0xC>(0u, x);      // rows 2, 3 add rows 0..1
+    return x;
 }
 
 // exclusive prefix sum over lanes
 __device__ __forceinline__ int wave_excl_scan(int v) {
-    const int lane = lane_id();
-    int x = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x - v;
+    return (int)wave_incl_scan((uint32_t)v) - v;
+}
+
+// wave-uniform sum over the 64 lanes
+__device__ __forceinline__ int wave_sum(int v) {
+    return (int)readlane(wave_incl_scan((uint32_t)v), 63);
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -173,28 +229,19 @@ struct LdsKeys {                      // keys buf[0..n) in LDS, strided over lan
 };
 
 // ---------------------------------------------------------------------------
-// Radix select of the rank-th largest (1-based) non-zero 64-bit key held by a
-// wave, MSB first over 8-bit digits.  `hist` is 256 u32 of LDS owned by this
-// wave.  Keys are unique, so the result is the exact rank-th key.  The result
-// is wave-uniform.  Requires 1 <= rank <= number of non-zero keys.
+// Radix threshold select over the non-zero 64-bit keys held by a wave (unique keys).
+// Returns a wave-uniform threshold th > 0 with
+//     rank <= #{keys >= th} <= keep_max        (1 <= rank <= keep_max, rank <= #keys)
+// keep_max == rank asks for exactly `rank` keys at or above th.  Digits are windows of
+// up to 8 bits, the first one just below the highest bit where the keys differ (the
+// bits above it are common to all keys and carry no information); each pass narrows
+// the window to the bin holding the rank-th key and stops as soon as keeping that
+// whole bin stays within keep_max.  `hist` is 256 u32 of LDS owned by this wave.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), off);
-        uint32_t hi = __shfl_xor((unsigned)(v >> 32), off);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o < v ? o : v;
-    }
-    return v;
-}
-
 template <class Src>
-__device__ uint64_t wave_select_kth(const Src& src, int rank, uint32_t* hist) {
+__device__ uint64_t wave_select_threshold(const Src& src, int rank, int keep_max,
+                                          uint32_t* hist) {
     const int lane = lane_id();
-    // Leading bytes shared by every key (those where the smallest and the largest key
-    // agree) hold no information: start below them.  Candidates above a threshold
-    // usually share their top score bytes, which would otherwise send every key to one
-    // histogram bin.
     uint64_t lo = ~0ull, hi = 0ull;
     src.for_each([&](uint64_t v) {
         if (v != 0ull) {
@@ -205,27 +252,26 @@ __device__ uint64_t wave_select_kth(const Src& src, int rank, uint32_t* hist) {
     lo = wave_min_u64(lo);
     hi = wave_max_u64(hi);
     const uint64_t diff = lo ^ hi;
-    if (diff == 0ull) return lo;              // a single distinct key
-    const int top = 63 - __clzll((long long)diff);   // highest differing bit
-    int shift = (top / 8) * 8;
-    uint64_t pmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+    if (diff == 0ull) return lo;                      // a single key
+    const int top = 63 - __clzll((long long)diff);    // highest differing bit
+    int shift = top >= 7 ? top - 7 : 0;               // window [shift, top]
+    int width = top - shift + 1;
+    uint64_t pmask = top == 63 ? 0ull : (~0ull << (top + 1));
     uint64_t prefix = lo & pmask;
-    for (; shift >= 0; shift -= 8) {
-        for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+    for (;;) {
+        *reinterpret_cast<u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
         wave_sync();
+        const uint32_t dmask = (1u << width) - 1u;
         src.for_each([&](uint64_t v) {
             if (v != 0ull && (v & pmask) == prefix)
-                atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
+                atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
         });
         wave_sync();
+        // lane l holds bins 4l..4l+3; keys in bins above lane l's: total - inclusive
         const u32x4 h = *reinterpret_cast<const u32x4*>(&hist[4 * lane]);
         const uint32_t local = h.x + h.y + h.z + h.w;
-        uint32_t suf = local;
-        for (int off = 1; off < 64; off <<= 1) {
-            uint32_t t = __shfl_down(suf, off);
-            if (lane + off < 64) suf += t;
-        }
-        uint32_t cum = suf - local;       // keys in higher bins (lanes above)
+        const uint32_t incl = wave_incl_scan(local);
+        uint32_t cum = readlane(incl, 63) - incl;
         int found = -1;
         uint32_t above_d = 0, cnt_d = 0;
         const uint32_t hb[4] = {h.x, h.y, h.z, h.w};
@@ -239,23 +285,28 @@ __device__ uint64_t wave_select_kth(const Src& src, int rank, uint32_t* hist) {
             cum += hb[b];
         }
         const uint64_t bal = __ballot(found >= 0);
-        const int srcl = __ffsll((long long)bal) - 1;
-        const int d = __shfl(found, srcl);
-        above_d = __shfl(above_d, srcl);
-        cnt_d = __shfl(cnt_d, srcl);
-        rank -= (int)above_d;
-        prefix |= (uint64_t)d << shift;
-        pmask |= 0xFFull << shift;
+        const int srcl = __builtin_amdgcn_readfirstlane(__ffsll((long long)bal) - 1);
+        const int d = (int)readlane((uint32_t)found, srcl);
+        above_d = readlane(above_d, srcl);
+        cnt_d = readlane(cnt_d, srcl);
         wave_sync();
-        if (cnt_d == 1u) {                // the rank-th key is the only one left
-            uint64_t best = 0;
-            src.for_each([&](uint64_t v) {
-                if (v != 0ull && (v & pmask) == prefix) best = v;
-            });
-            return wave_max_u64(best);
-        }
+        rank -= (int)above_d;
+        keep_max -= (int)above_d;
+        prefix |= (uint64_t)d << shift;
+        pmask |= (uint64_t)dmask << shift;
+        // keeping the whole bin stays within keep_max: done.  This always happens by
+        // the last window (bit 0), where a bin is a single key value: rank <= cnt_d
+        // <= 1 <= keep_max.
+        if ((int)cnt_d <= keep_max || shift == 0) return prefix;
+        width = shift >= 8 ? 8 : shift;
+        shift -= width;
     }
-    return prefix;
+}
+
+// The rank-th largest key's threshold: exactly `rank` keys are >= the result.
+template <class Src>
+__device__ __forceinline__ uint64_t wave_select_kth(const Src& src, int rank, uint32_t* hist) {
+    return wave_select_threshold(src, rank, rank, hist);
 }
 
 }  // namespace si

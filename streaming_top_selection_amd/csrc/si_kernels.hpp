@@ -60,6 +60,9 @@ struct MatSelectArgs {
 
 hipError_t launch_select(const SelectArgs& a, int nwave, int kb, int nsub, int cg, bool fp8,
                          hipStream_t stream);
+// one register-tile shape (NWAVE waves x KB blocks x NSUB register tiles per key tile)
+template <int NWAVE, int KB, int NSUB, bool FP8>
+hipError_t launch_select_shape(const SelectArgs& a, int cg, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_mat_score(const MatScoreArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_mat_select(const MatSelectArgs& a, hipStream_t stream);

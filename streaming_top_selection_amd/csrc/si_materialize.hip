@@ -10,12 +10,13 @@ namespace si {
 
 // ---- score write-out: one workgroup = 32 rows x 512 keys --------------------------
 template <bool FP8>
-__global__ void __launch_bounds__(512) mat_score_kernel(MatScoreArgs A) {
-    constexpr int NWAVE = 8, KB = 2, RT = NWAVE * KB * kMB;
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mat_score_kernel(MatScoreArgs A) {
+    constexpr int NWAVE = 4, KB = 4, RT = NWAVE * KB * kMB;
     __shared__ ScoreLds L;
     SI_DECLARE_QBUFS(Q);
     const Problem& P = A.P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
 
     int64_t id = blockIdx.x;
     const int64_t b = id % P.B;
@@ -34,18 +35,20 @@ __global__ void __launch_bounds__(512) mat_score_kernel(MatScoreArgs A) {
         __syncthreads();
         score_regs<NWAVE, KB, FP8>(P, b, trow0, rows_valid, key0, L, Q, acc);
     }
-    const int qj = lane & 31;
-    const int64_t row = trow0 + qj;
-    if (qj >= rows_valid || row < A.row0 || row >= A.row0 + A.rows) return;
-    const int64_t nvis = visible_keys(P.q_pos0 + row, P.m, P.T);
-    float* out = A.scores + (b * A.rows + (row - A.row0)) * P.T;
+    // register r holds row trow0 + mfma_row(r, lane); lanes run along the keys, so
+    // each store writes 32 consecutive scores of two rows
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int r = 0; r < 16; ++r) {
+        const int64_t row = trow0 + mfma_row(r, lane);
+        if (row >= trow0 + rows_valid || row < A.row0 || row >= A.row0 + A.rows) continue;
+        const int64_t nvis = visible_keys(P.q_pos0 + row, P.m, P.T);
+        float* out = A.scores + (b * A.rows + (row - A.row0)) * P.T;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t s = key0 + (int64_t)(wave * KB + kb) * kMB + mfma_row(r, lane);
+        for (int kb = 0; kb < KB; ++kb) {
+            const int64_t s = key0 + (int64_t)(wave * KB + kb) * kMB + (lane & 31);
             if (s < P.T) out[s] = (live && s < nvis) ? acc[kb][r] : -__builtin_inff();
         }
+    }
 }
 
 // ---- exact selection from one written score row: one 64-lane group per row -------
@@ -135,9 +138,9 @@ hipError_t launch_mat_score(const MatScoreArgs& a, bool fp8, hipStream_t stream)
     const int64_t grid = (int64_t)a.n_row_tiles * a.n_key_tiles * a.P.B;
     if (grid <= 0) return hipSuccess;
     if (fp8)
-        hipLaunchKernelGGL(mat_score_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL(mat_score_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(mat_score_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL(mat_score_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -72,10 +72,10 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
     switch (kt) {
         case 64:   pl.nwave = 2; pl.kb = 1; pl.nsub = 1; break;
         case 128:  pl.nwave = 4; pl.kb = 1; pl.nsub = 1; break;
-        case 256:  pl.nwave = 8; pl.kb = 1; pl.nsub = 1; break;
-        case 512:  pl.nwave = 8; pl.kb = 2; pl.nsub = 1; break;
-        case 768:  pl.nwave = 4; pl.kb = 6; pl.nsub = 1; break;
-        case 1024: pl.nwave = 8; pl.kb = 2; pl.nsub = 2; break;
+        case 256:  pl.nwave = 4; pl.kb = 2; pl.nsub = 1; break;
+        case 512:  pl.nwave = 4; pl.kb = 4; pl.nsub = 1; break;
+        case 768:  pl.nwave = 4; pl.kb = 2; pl.nsub = 3; break;
+        case 1024: pl.nwave = 4; pl.kb = 4; pl.nsub = 2; break;
         default:
             msg = "key_tile must be 64, 128, 256, 512, 768 or 1024"; return SI_ERR_UNSUPPORTED;
     }

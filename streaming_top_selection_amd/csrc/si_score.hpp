@@ -9,15 +9,23 @@
 // (indexer score: per-head dot, ReLU, head-weighted sum; the pages give no formula.)
 //
 // Data flow (MI355X layout, not the pages' Triton design):
-//  * K-stationary: each wave loads its keys once into MFMA A-operand registers and
-//    keeps them for all heads (a key tile is the same for every head).
+//  * K-stationary: each wave loads its keys once into MFMA B-operand registers and
+//    keeps them for all heads (a key tile is the same for every head).  With one
+//    wave per SIMD a wave has 512 registers, so KB = 4 blocks of 32 keys fit beside
+//    double-buffered q operands without spilling.
 //  * q is streamed head by head into LDS tiles of 32 rows x 128 bf16 (8 KiB/head) by
-//    direct global->LDS loads issued several heads ahead (no register staging);
-//    all waves of the workgroup share each tile as the MFMA B operand.
-//  * Software pipeline: the MFMAs of head h+1 are issued interleaved with the VALU
-//    epilogue (ReLU, weighted sum) of head h, so both pipes stay busy in each wave.
-//  * Output layout: lane l owns query column (l & 31) and key rows mfma_row(r, l),
-//    so the head weight w[t,h] is one LDS read per lane per head.
+//    buffer->LDS loads issued several heads ahead (no register staging, two loads
+//    per wave and head, no branches); all waves of the workgroup share each tile as
+//    the MFMA A operand.
+//  * Software pipeline: the MFMAs of the next block are issued interleaved with the
+//    VALU epilogue (ReLU, weighted sum) of the current one, so both pipes stay busy
+//    in each wave; the LDS reads of head h+1 and the loads of head h+7 are issued in
+//    the shadow of step h's MFMAs, so only the barrier sits between the last MFMA of
+//    a step and the first of the next.
+//  * Output layout: queries are MFMA rows and keys columns, so lane l owns key
+//    (l & 31) of each block and query rows mfma_row(r, l).  A query's scores for
+//    32 consecutive keys sit in one register across 32 lanes, which lets the
+//    selection append survivors as contiguous runs.
 #pragma once
 
 #include <type_traits>
@@ -37,20 +45,19 @@ struct Problem {
 };
 
 constexpr int kQBuf = 8;             // q tiles in flight: head h+7 loads while h+1 is read
-constexpr int kWStride = kMaxH + kQBuf + 1;  // w row: H weights, zero pad, odd stride
-constexpr int kQRowSlots = 17;       // 16-byte slots per staged q row: 16 data + 1 pad
-constexpr int kQRow = kQRowSlots * 8;        // staged q row in bf16 (272 bytes)
-constexpr int kQSlots = kTQ * kQRowSlots;    // 16-byte slots per staged q tile
-constexpr int kQTile = kTQ * kQRow;          // bf16 per staged q tile
+constexpr int kWHeads = kMaxH + kQBuf;       // weight rows: H heads, then zeros
+constexpr int kQChunks = kTQ * 16;   // 16-byte chunks per staged q tile (32 rows x 256 B)
+constexpr int kQTile = kQChunks * 8;         // bf16 per staged q tile (8 KiB)
 
 struct ScoreLds {
-    float w[kTQ * kWStride];      // head weights of the 32 query rows (0 past H)
+    float w[kWHeads * kTQ];       // [head][query row] weights (0 past H or the tile's rows)
 };
 
 // The staged q tiles: kQBuf separate LDS arrays (each its own object, so the
-// compiler can tell the direct-to-LDS loads into one from reads of another).  Row j
-// of a tile starts at 16-byte slot 17*j, so the B-operand reads (16 rows at a time,
-// the same 16-byte piece of each) hit 16 different bank groups.
+// compiler can tell the direct-to-LDS loads into one from reads of another).  Chunk c
+// (d = 8c .. 8c+7) of row r sits at chunk 16*r + (c ^ (r & 15)) of the tile, so an
+// A-operand read (16 consecutive rows at a time, the same chunk of each) hits 16
+// different 16-byte bank groups.
 struct QBufs {
     uint16_t* p[kQBuf];
 };
@@ -76,21 +83,42 @@ __device__ __forceinline__ void loop_barrier() {
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding).
 #define SI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | 0x70 | 0xF00)
 
-// Fills L.w for query rows [row0, row0 + rows_valid) of batch entry b (0 past the end).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// buffer_load_dwordx4 ... lds: lane L's 16 bytes at rsrc.base + voffset go to LDS at
+// lds + 16*L (the LDS address is taken from M0, so it is wave-uniform).
+extern "C" __device__ void si_raw_buffer_load_lds(
+    i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size, int voffset,
+    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer resource (gfx9): 48-bit base, stride 0, num_records bytes; reads past
+// num_records return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(uint64_t base, uint32_t num_records) {
+    i32x4 r;
+    r.x = (int32_t)(uint32_t)base;
+    r.y = (int32_t)((uint32_t)(base >> 32) & 0xFFFFu);
+    r.z = (int32_t)num_records;
+    r.w = 0x00020000;
+    return r;
+}
+
+// Fills L.w for query rows [row0, row0 + rows_valid) of batch entry b (0 past the end):
+// read along rows of w (coalesced), stored transposed, one head per LDS row.
 template <int NT>
 __device__ __forceinline__ void load_w_tile(const Problem& P, int64_t b, int64_t row0,
                                             int rows_valid, ScoreLds& L) {
     const int H = P.H;
-    for (int f = threadIdx.x; f < kTQ * kWStride; f += NT) {
-        const int j = f / kWStride, h = f - j * kWStride;
-        L.w[f] = (j < rows_valid && h < H) ? P.w[((b * P.S + row0 + j) * H) + h] : 0.0f;
+    for (int f = threadIdx.x; f < kTQ * kWHeads; f += NT) {
+        const int j = f / kWHeads, h = f - j * kWHeads;
+        L.w[h * kTQ + j] = (j < rows_valid && h < H) ? P.w[((b * P.S + row0 + j) * H) + h] : 0.0f;
     }
 }
 
 // Scores rows [row0, row0 + rows_valid) against keys key0 + [0, NWAVE*KB*32).
 // Requires: L.w filled and a __syncthreads() since; key0 % 32 == 0; every thread of
-// the workgroup calls it.  acc[kb][r] receives the score of query (lane & 31) and key
-// key0 + (wave*KB + kb)*32 + mfma_row(r, lane).  Keys >= T score as if zero.
+// the workgroup calls it.  acc[kb][r] receives the score of query row
+// row0 + mfma_row(r, lane) and key key0 + (wave*KB + kb)*32 + (lane & 31).  Keys >= T
+// score as if zero.
 template <int NWAVE, int KB, bool FP8>
 __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t row0,
                                            int rows_valid, int64_t key0, ScoreLds& L,
@@ -100,12 +128,12 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int hh = lane >> 5;       // which 64-wide half of d this lane feeds
-    const int il = lane & 31;       // A row (key) and B column (query) of this lane
+    const int il = lane & 31;       // A row (query) and B column (key) of this lane
     const int H = P.H;
 
-    // ---- K fragments: keys stay in registers for the whole head loop ----------
+    // ---- K fragments (B operand): keys stay in registers for the whole head loop ----
     // step s covers d = 64*hh + 8*s + [0, 8) for lane l (same d for A and B).
     bf16x8 kf[KB][8];
 #pragma unroll
@@ -138,64 +166,78 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
         }
     }
 
-    // ---- q staging: direct global -> LDS loads, kQBuf - 2 heads ahead ----------
-    // Slot t of a head's tile (row t / 17, piece t % 17; piece 16 is the row pad and
-    // receives a copy of piece 15) is filled by thread t mod NT in round t / NT; each
-    // wave instruction writes 64 consecutive slots, as the LDS-DMA load requires.
-    // Rows past the tile's end re-load the last valid row (weights 0, never selected)
-    // and heads past H-1 re-load head H-1, so every step issues the same loads.
-    constexpr int QPER = (kQSlots + NT - 1) / NT;
-    // loads per head issued by the wave with the fewest (the last one)
-    constexpr int QMIN = ((kQSlots - (NWAVE - 1) * 64) + NT - 1) / NT;
+    // ---- q staging: buffer -> LDS loads, kQBuf - 2 heads ahead -----------------
+    // In each of QN rounds a wave loads 64 consecutive chunks of the tile: chunk P =
+    // n*NT + tid holds row r = P / 16, piece c = (P % 16) ^ (r & 15).  Rows past the
+    // tile's end re-load its last row (weight 0, never selected); heads past H-1
+    // re-load head H-1, so every step issues the same loads.  The resource covers this
+    // tile's rows; its base moves by one head per load.
+    constexpr int QN = kQChunks / NT;
+    static_assert(kQChunks % NT == 0, "every wave issues the same number of q loads");
     constexpr int AHEAD = kQBuf - 2;
-    int64_t qoff[QPER];
+    const uint64_t qbase = reinterpret_cast<uint64_t>(P.q + (b * P.S + row0) * H * (int64_t)kD);
+    const uint32_t qbytes = (uint32_t)(rows_valid * H * kD * 2);
+    int voff[QN];
 #pragma unroll
-    for (int n = 0; n < QPER; ++n) {
-        const int slot = tid + n * NT;
-        const int jr = slot / kQRowSlots;
-        const int c = min(slot - jr * kQRowSlots, 15);
-        const int j = min(jr, rows_valid - 1);
-        qoff[n] = ((b * P.S + row0 + j) * H) * (int64_t)kD + c * 8;
+    for (int n = 0; n < QN; ++n) {
+        const int chunk = n * NT + tid;
+        const int r = chunk >> 4;
+        const int c = (chunk & 15) ^ (r & 15);
+        voff[n] = (min(r, rows_valid - 1) * H * kD + c * 8) * 2;
     }
     auto qload = [&](uint16_t* buf, int h) {
-        const int64_t hc = h < H ? h : H - 1;
+        const uint32_t hc = (uint32_t)(h < H ? h : H - 1);
+        const i32x4 rsrc = make_rsrc(qbase + hc * (kD * 2), qbytes - hc * (kD * 2));
 #pragma unroll
-        for (int n = 0; n < QPER; ++n) {
-            const int base = wave * 64 + n * NT;          // first slot of this wave's row
-            if (base < kQSlots && base + lane < kQSlots) {
-                __builtin_amdgcn_global_load_lds(
-                    (__attribute__((address_space(1))) void*)(P.q + qoff[n] + hc * kD),
-                    (__attribute__((address_space(3))) void*)(buf + base * 8), 16, 0, 0);
-            }
-        }
+        for (int n = 0; n < QN; ++n)
+            si_raw_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(buf + (n * NT + wave * 64) * 8),
+                16, voff[n], 0, 0, 0);
     };
-    auto qread = [&](const uint16_t* buf, bf16x8 (&bq)[8]) {
-        const uint16_t* row = buf + il * kQRow + 64 * hh;
+    // A operand of one head: query row il, d = 64*hh + 8*s + [0, 8), i.e. piece 8*hh + s
+    int roff[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(row + 8 * s);
+    for (int s = 0; s < 8; ++s) roff[s] = il * 256 + 16 * ((8 * hh + s) ^ (il & 15));
+    auto qread = [&](const uint16_t* buf, bf16x8 (&bq)[8], int s0, int s1) {
+        const char* base = reinterpret_cast<const char*>(buf);
+#pragma unroll
+        for (int s = s0; s < s1; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(base + roff[s]);
     };
-    // MFMA chain of key block kb for one head: z = A(kb) * B over d, from zero
+    // head weights of this lane's 16 query rows: rows 8*g + 4*hh + [0, 4), g = 0..3
+    // (one 16-byte LDS read per g; the 32 lanes of a half read the same address)
+    auto wread = [&](int h, f32x4 (&wv)[4]) {
+        const f32x4* row = reinterpret_cast<const f32x4*>(L.w + h * kTQ + 4 * hh);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) wv[g] = row[2 * g];
+    };
+    // MFMA chain of key block kb for one head: z = Q_h * K(kb)^T over d, from zero
     auto mfma_block = [&](int kb, const bf16x8 (&bq)[8], f32x16& z) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) z[r] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) z = mfma32x32x16(kf[kb][s], bq[s], z);
+        for (int s = 0; s < 8; ++s) z = mfma32x32x16(bq[s], kf[kb][s], z);
     };
-    auto epilogue_block = [&](int kb, const f32x16& z, float wh) {
+    auto epilogue_block = [&](int kb, const f32x16& z, const f32x4 (&wv)[4]) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            acc[kb][r] = __builtin_fmaf(wh, __builtin_fmaxf(z[r], 0.0f), acc[kb][r]);
+            acc[kb][r] = __builtin_fmaf(wv[r >> 2][r & 3], __builtin_fmaxf(z[r], 0.0f),
+                                        acc[kb][r]);
     };
     // Keeps an accumulator block's epilogue inside the step that issues it (without
     // this the compiler sinks every epilogue of the unrolled loop to its end and keeps
     // all their MFMA outputs alive at once).
     auto pin = [&](f32x16& v) { asm volatile("" : "+v"(v)); };
-    // one MFMA block (8 MFMAs) interleaved with one epilogue block (32 VALU)
-    auto interleave = [&]() {
+    // one MFMA block (8 MFMAs) interleaved with one epilogue block (32 VALU), with
+    // a share of the step's 12 LDS reads (RD[kb] of them, one per MFMA) and, in block
+    // KLOAD, its q loads
+    constexpr int KLOAD = KB > 1 ? 1 : 0;
+    auto interleave = [&](int kb, int nread) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+            if (i < nread) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (kb == KLOAD && i < QN) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
 
@@ -208,8 +250,9 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     // (0,0), (0,1), ..., (0,KB-1), (1,0), ...: the MFMA chain of block X + ZR - 1 is
     // issued interleaved with the epilogue (ReLU, weighted sum) of block X, so an
     // epilogue never waits on a chain that was just issued, and block X lives in
-    // accumulator slot X mod ZR.  The B operand of head h+1 (bq[(h+1) % 2]) is read at
-    // the start of step h, ahead of its first use.
+    // accumulator slot X mod ZR.  The A operand and the weights of head h+1
+    // (bq[(h+1) % 2], wv[(h+1) % 2]) are read at the top of step h, ahead of their
+    // first use, and a scheduling barrier keeps those reads there.
     //
     // Step h (buffers known at compile time): read head h+1 from buffer (h+1) % 8;
     // for kb = 0..KB-1 run the MFMAs of block (h, kb) + ZR - 1 beside the epilogue of
@@ -223,26 +266,37 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     static_assert(LA <= KB, "lookahead stays within the next head");
     f32x16 z[ZR];
     bf16x8 bq[2][8];
+    f32x4 wv[2][4];
     auto step = [&](auto rstep, int h) {
         constexpr int R = decltype(rstep)::value;            // h mod 8
         constexpr int RB = (R + 1) % kQBuf, LB = (R + kQBuf - 1) % kQBuf;
         constexpr int C = R % 2, N = 1 - C;
-        const float wh = L.w[il * kWStride + h];
-        qread(Q.p[RB], bq[N]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int x = R * KB + kb;                        // block index mod 8*KB
             const int ykb = (kb + LA) % KB;                   // block x + LA
             const bool next_head = kb + LA >= KB;
+            // reads of head h+1 (first used by the block of head h+1, the last one):
+            // spread over the blocks before it, at most one per MFMA
+            int nread = 0;
+            if (KB >= 3) {
+                if (kb == 0) qread(Q.p[RB], bq[N], 0, 4), nread = 4;
+                if (kb == 1) qread(Q.p[RB], bq[N], 4, 8), nread = 4;
+                if (kb == 2) wread(h + 1, wv[N]), nread = 4;
+            } else if (kb == 0) {
+                qread(Q.p[RB], bq[N], 0, 8);
+                wread(h + 1, wv[N]);
+                nread = 8;
+            }
+            if (kb == KLOAD) qload(Q.p[LB], h + AHEAD + 1);
             mfma_block(ykb, next_head ? bq[N] : bq[C], z[(x + LA) % ZR]);
-            epilogue_block(kb, z[x % ZR], wh);
-            interleave();
+            epilogue_block(kb, z[x % ZR], wv[C]);
+            interleave(kb, nread);
             pin(acc[kb]);
         }
-        qload(Q.p[LB], h + AHEAD + 1);
-        // head h+2 (read in step h+1) must have landed: every wave issues at least
-        // QMIN loads per head, so <= (AHEAD-1)*QMIN younger loads means it has
-        SI_WAIT_VMCNT((AHEAD - 1) * QMIN);
+        // head h+2 (read in step h+1) must have landed: every wave issues QN loads
+        // per head, so <= (AHEAD-1)*QN younger loads means it has
+        SI_WAIT_VMCNT((AHEAD - 1) * QN);
         loop_barrier();
     };
     using I0 = std::integral_constant<int, 0>;
@@ -263,9 +317,10 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     qload(Q.p[4], 4);
     qload(Q.p[5], 5);
     qload(Q.p[6], 6);
-    SI_WAIT_VMCNT((AHEAD - 1) * QMIN);
+    SI_WAIT_VMCNT((AHEAD - 1) * QN);
     loop_barrier();
-    qread(Q.p[0], bq[0]);
+    qread(Q.p[0], bq[0], 0, 8);
+    wread(0, wv[0]);
 #pragma unroll
     for (int x = 0; x < LA; ++x) mfma_block(x, bq[0], z[x]);   // blocks (0, 0..LA-1)
 
@@ -283,15 +338,22 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     // the last steps' loads (of padding heads) land before anything else uses LDS
     SI_WAIT_VMCNT(0);
 
+    float kscale[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        kscale[kb] = 1.0f;
+        if constexpr (FP8) {
+            const int64_t key = key0 + (int64_t)(wave * KB + kb) * kMB + il;
+            if (key < P.T) kscale[kb] = P.kc_scale[b * P.T + key];
+        }
+    }
+
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float v = acc[kb][r];
-            if constexpr (FP8) {
-                const int64_t key = key0 + (int64_t)(wave * KB + kb) * kMB + mfma_row(r, lane);
-                v = v * (key < P.T ? P.kc_scale[b * P.T + key] : 1.0f);
-            }
+            if constexpr (FP8) v = v * kscale[kb];
             acc[kb][r] = canon_zero(v);
         }
     }

@@ -1,0 +1,7 @@
+// Select kernels for key tile 1024 (4 waves x 4 blocks x 2 register tiles), e4m3 keys.
+#include "si_select.hpp"
+
+namespace si {
+template hipError_t launch_select_shape<4, 4, 2, true>(const SelectArgs&, int,
+                                                              hipStream_t);
+}  // namespace si

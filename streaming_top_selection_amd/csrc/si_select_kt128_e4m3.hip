@@ -1,0 +1,7 @@
+// Select kernels for key tile 128 (4 waves x 1 blocks x 1 register tiles), e4m3 keys.
+#include "si_select.hpp"
+
+namespace si {
+template hipError_t launch_select_shape<4, 1, 1, true>(const SelectArgs&, int,
+                                                              hipStream_t);
+}  // namespace si

@@ -1,0 +1,7 @@
+// Select kernels for key tile 256 (4 waves x 2 blocks x 1 register tiles), bf16 keys.
+#include "si_select.hpp"
+
+namespace si {
+template hipError_t launch_select_shape<4, 2, 1, false>(const SelectArgs&, int,
+                                                              hipStream_t);
+}  // namespace si
