@@ -6,6 +6,8 @@
 #include "si_kernels.hpp"
 #include "si_plan.hpp"
 
+static_assert(si::kCandPad == si::kPlanCandPad, "candidate list padding");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -111,7 +113,7 @@ si_status run_merge(const si::PlanInternal& pl, int64_t B, int64_t S, int64_t T,
     a.P_chunk = si::chunk_partitions(pl, S, T, m, q_pos0, chunk);
     a.P_ws = pl.pub.n_partitions;
     a.QC = pl.pub.query_chunk;
-    a.CG = pl.pub.cand_capacity;
+    a.CG = pl.pub.cand_capacity + si::kPlanCandPad;   // list stride
     a.KP = pl.pub.key_partition;
     a.cand = static_cast<const uint64_t*>(ws);
     a.cnt = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + pl.cand_bytes);

@@ -18,6 +18,9 @@ constexpr int kMB = 32;          // keys per MFMA block = MFMA M
 constexpr int kMaxH = 128;       // most indexer heads supported
 constexpr int kMaxK = 2048;      // largest top-k supported
 constexpr int kWave = 64;
+// Slots after each candidate list that absorb the stores of lanes with nothing to
+// write, so that appends and compactions store with no branch (never read).
+constexpr int kCandPad = 64;
 
 // ---------------------------------------------------------------------------
 // MFMA: D[32x32] = A[32x16] * B[16x32] + C, bf16 inputs, fp32 accumulation.

@@ -165,9 +165,9 @@ __device__ __forceinline__ void load_keys(const uint64_t* buf, uint64_t (&v)[E])
 }
 
 // Keeps between k and keep_max of the largest of the cnt keys v (exactly k when
-// keep_max == k; 1 <= k < cnt; keep_max <= E*64 - 64), written back to buf[0, kept) as
-// contiguous runs; the dropped keys go to the last 64 slots, so every store is issued
-// with no branch.  Slots of v past cnt are ignored.  Returns the kept count; *th_ord
+// keep_max == k; 1 <= k < cnt), written back to buf[0, kept) as contiguous runs; the
+// dropped keys go to the kCandPad slots after the list (buf[E*64, E*64 + 64)), so every
+// store is issued with no branch.  Slots of v past cnt are ignored.  Returns the kept count; *th_ord
 // receives the smallest kept key's score image.
 template <int E>
 __device__ __forceinline__ int compact_regs(uint64_t* buf, uint64_t (&v)[E], int cnt,
@@ -226,7 +226,7 @@ __device__ __forceinline__ int compact_regs(uint64_t* buf, uint64_t (&v)[E], int
         const uint64_t m = __ballot(keep);
         const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
                                   (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        buf[keep ? at : E * 64 - 64 + lane] = v[e];
+        buf[keep ? at : E * 64 + lane] = v[e];
         const uint32_t o = (uint32_t)(v[e] >> 32);
         tmin = keep && o < tmin ? o : tmin;
         base += __popcll(m);

@@ -19,7 +19,7 @@ struct SelectArgs {
     int32_t P_ws;                     // partition stride of the workspace
     int32_t QC;                       // row stride of the workspace (query_chunk)
     int64_t KP;                       // keys per partition
-    uint64_t* cand;                   // [B][QC][P_ws][CG] selection keys
+    uint64_t* cand;                   // [B][QC][P_ws][CG + kCandPad] selection keys
     int32_t* cnt;                     // [B][QC][P_ws] list lengths (<= k when done)
 };
 
@@ -29,7 +29,7 @@ struct MergeArgs {
     int32_t m, k;
     int64_t q_pos0;
     int64_t chunk_row0, chunk_row1;
-    int32_t P_chunk, P_ws, QC, CG;
+    int32_t P_chunk, P_ws, QC, CG;   // CG: list stride (capacity + kCandPad)
     int64_t KP;
     const uint64_t* cand;
     const int32_t* cnt;

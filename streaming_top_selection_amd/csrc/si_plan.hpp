@@ -18,6 +18,7 @@ constexpr int32_t kMaxPartitions = 64;       // lists one merge wave gathers
 constexpr int64_t kMergeMaxEntries = 8192;   // 64 KiB of LDS keys in the merge
 constexpr int64_t kAutoWorkspaceCap = int64_t(3) << 29;   // 1.5 GiB: auto query_chunk bound
 constexpr int32_t kTargetGroups = 1024;      // workgroups one select launch aims for
+constexpr int32_t kPlanCandPad = 64;         // unread slots after each candidate list
 
 struct PlanInternal {
     si_plan pub;
@@ -112,7 +113,7 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
     }
 
     // query chunk
-    const int64_t per_row = B * nparts * (int64_t(cg) * 8 + 4);
+    const int64_t per_row = B * nparts * (int64_t(cg + kPlanCandPad) * 8 + 4);
     int64_t qc;
     if (c.query_chunk) {
         qc = round_up(c.query_chunk, kPlanTQ);
@@ -124,7 +125,7 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
     if (qc > (int64_t(1) << 30)) { msg = "query_chunk too large"; return SI_ERR_UNSUPPORTED; }
     const int64_t nchunks = S == 0 ? 0 : ceil_div(S, qc);
 
-    const int64_t cand_bytes = round_up(B * qc * nparts * int64_t(cg) * 8, 256);
+    const int64_t cand_bytes = round_up(B * qc * nparts * int64_t(cg + kPlanCandPad) * 8, 256);
     const int64_t cnt_bytes = round_up(B * qc * nparts * 4, 256);
 
     pl.pub.key_tile = kt;

@@ -122,7 +122,11 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
     }
     int my_base = 0;
     if (lane < kTQ && my_count > 0) my_base = atomicAdd(&sCnt[lane], my_count);
-    // pass 2: write each (register, block) as one run per half
+    // pass 2: write each (register, block) as one run per half; every lane stores
+    // (lanes with no survivor into the list's pad slots), so no store needs a branch
+    uint32_t low[KB];                       // key low bits: ~index
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) low[kb] = ~(uint32_t)(kbase + kb * kMB + il);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int q_lo = mfma_row(r, 0), q_hi = mfma_row(r, 32);
@@ -140,8 +144,9 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
                 m_hi, upper ? 0u : __builtin_amdgcn_mbcnt_lo(m_lo, 0u));
             const int at = (upper ? b_hi : b_lo) + below;
             // the compaction policy keeps every position below CG; the bound only keeps
-            // a broken invariant from writing outside this query's buffer
-            if (pass && at < CG) row[at] = make_key(acc[kb][r], (uint32_t)(kbase + kb * kMB + il));
+            // a broken invariant from writing outside this query's list
+            const int dst = pass && at < CG ? at : CG + il;
+            row[dst] = ((uint64_t)ord_f32(acc[kb][r]) << 32) | low[kb];
             b_lo += __popc(m_lo);
             b_hi += __popc(m_hi);
         }
@@ -186,6 +191,7 @@ select_kernel(SelectArgs A) {
     const int64_t key_lo = (int64_t)p * A.KP;
     const int64_t key_hi = min(key_lo + A.KP, n_last);
     const int64_t slot0 = (b * A.QC + (row0 - A.chunk_row0)) * A.P_ws + p;
+    constexpr int CGS = CG + kCandPad;     // list stride
 
     if (key_lo >= key_hi) {
         if (tid < rows_valid) A.cnt[slot0 + (int64_t)tid * A.P_ws] = 0;
@@ -201,7 +207,7 @@ select_kernel(SelectArgs A) {
     __syncthreads();
     // keys below this bound are visible to every row of the tile and inside the partition
     const int64_t all_visible = min(visible_keys(t0, P.m, P.T), key_hi);
-    const int64_t row_stride = (int64_t)A.P_ws * CG;
+    const int64_t row_stride = (int64_t)A.P_ws * CGS;
     // keys a mid-partition compaction may keep: k plus a quarter of the free room
     const int keep_mid = A.k + (CG - KT - A.k) / 4;
 
@@ -211,7 +217,7 @@ select_kernel(SelectArgs A) {
         score_regs<NWAVE, KB, FP8>(P, b, row0, rows_valid, key0, L, Q, acc);
 
         const int64_t kbase = key0 + (int64_t)wave * KB * kMB;
-        uint64_t* const cand_tile = A.cand + slot0 * CG;
+        uint64_t* const cand_tile = A.cand + slot0 * CGS;
         if (kbase + KB * kMB <= all_visible)
             filter_append<KB, CG, false>(acc, kbase, sThf, sN, sCnt, cand_tile, row_stride);
         else
@@ -236,7 +242,7 @@ select_kernel(SelectArgs A) {
                 __syncthreads();
                 // rows wave, wave + NWAVE, ... of the tile are this wave's
                 const uint64_t todo = __ballot(c > limit && lane % NWAVE == wave);
-                compact_rows<E, CG>(todo, A.cand + slot0 * CG, row_stride, A.k, keep_max, sCnt,
+                compact_rows<E, CG>(todo, A.cand + slot0 * CGS, row_stride, A.k, keep_max, sCnt,
                                     sThf, sHist[wave], sStage[wave]);
                 __syncthreads();
             }

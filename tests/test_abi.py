@@ -58,9 +58,10 @@ def test_plan_headline_workload_is_one_chunk_one_partition(lib):
     p = plan()
     assert p.n_chunks == 1 and p.query_chunk == 65536 and p.n_partitions == 1
     assert p.key_tile == 512 and p.cand_capacity == 2048
-    # candidate keys + counts for every query row, 256-byte aligned parts
-    assert p.workspace_bytes >= 65536 * 2048 * 8 + 65536 * 4
-    assert p.workspace_bytes < 65536 * 2048 * 8 + 65536 * 4 + 512
+    # candidate keys (2048 slots + 64 pad slots per list) + counts for every query row,
+    # 256-byte aligned parts
+    assert p.workspace_bytes >= 65536 * (2048 + 64) * 8 + 65536 * 4
+    assert p.workspace_bytes < 65536 * (2048 + 64) * 8 + 65536 * 4 + 512
 
 
 def test_plan_million_token_workspace_is_bounded():
