@@ -126,7 +126,11 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     constexpr int NT = NWAVE * kWave;
     static_assert(kQBuf >= 4, "the pipeline reads head h+1 while loading h+kQBuf-1");
 
-    const int tid = threadIdx.x;
+    // The empty asm makes every per-lane value below (load and read offsets) a fresh
+    // computation at each call: hoisted out of the caller's key loop they would stay
+    // live through its selection code and crowd the head loop's registers.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = wave_id();
     const int hh = lane >> 5;       // which 64-wide half of d this lane feeds

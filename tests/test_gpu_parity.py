@@ -111,14 +111,16 @@ def test_ragged_every_row(gpu_lib, q_pos0):
                       oa["w"], spec.m, q_pos0=q_pos0, b=1)
 
 
-def test_odd_heads_and_ratio(gpu_lib):
-    """H = 3 heads, m = 1 (every earlier key visible), k above most rows' counts."""
-    spec = synth.InputSpec(B=1, S=300, T=300, H=3, m=1, k=100, seed=22)
-    say("odd heads")
+@pytest.mark.parametrize("H,S,key_tile", [(3, 300, 512), (5, 1100, 512), (13, 700, 64)])
+def test_odd_heads_and_ratio(gpu_lib, H, S, key_tile):
+    """Head counts that are not a multiple of 8, m = 1 (every earlier key visible), and
+    rows whose keys span several register tiles (the q pipeline carried across tiles)."""
+    spec = synth.InputSpec(B=1, S=S, T=S, H=H, m=1, k=100, seed=22 + H)
+    say("odd heads", H, S, key_tile)
     xc = synth.make_inputs(spec)
     xd = dev(xc)
     oa = oracle_args(xc, spec)
-    gi, gs = run_stream(gpu_lib, xd, 1, 100)
+    gi, gs = run_stream(gpu_lib, xd, 1, 100, key_tile=key_tile)
     check_rows(gi[0].cpu().numpy(), gs[0].cpu().numpy(), range(spec.S), oa["q_bits"],
                oa["kc_bits"], oa["w"], 1, 100)
     assert_same((gi, gs), run_mat(gpu_lib, xd, 1, 100), "odd heads")
