@@ -4,8 +4,8 @@
 // into the final top-k with no global sort of the scores (geoz.com.cn page, FAQ;
 // jeff.news page, sequence diagram: merge-topk keeps the final top-k).
 //
-// One 64-lane workgroup per query row.  The lists (at most partitions * k keys,
-// bounded by the planner to 8192) are gathered into LDS; if they hold more than k
+// General case, one 64-lane workgroup per query row: the lists (at most partitions *
+// k keys, bounded by the planner to 8192) are gathered into LDS; if they hold more than k
 // keys an exact radix select finds the k-th key and an in-place compaction keeps the
 // top k; a bitonic sort orders them.  HBM traffic: read the lists, write the row.
 #include "si_kernels.hpp"
@@ -91,10 +91,139 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeArgs A) {
     }
 }
 
+// ---- one partition per row and k <= 512: a register sort -----------------------
+// The row's single list already holds its top-k (the select stage compacted it to at
+// most k keys), so the merge is a sort.  One wave per row; lane l holds elements
+// 8l .. 8l+7 of a 512-key bitonic network (padding keys are 0, below every real
+// key), so strides 1, 2, 4 compare within a lane and strides 8 .. 256 against lane
+// l ^ (stride / 8).  Loads and stores are contiguous 64-byte runs per lane.
+constexpr int kSortN = 512;
+constexpr int kSortWaves = 4;
+
+// 64-bit lane exchange: partner lane ^ m (DPP within a quad for m = 1, 2)
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+    if constexpr (M == 1 || M == 2) {
+        constexpr int C = M == 1 ? kDppQuadSwap1 : kDppQuadSwap2;
+        const uint32_t lo = dpp<C>(0u, (uint32_t)v), hi = dpp<C>(0u, (uint32_t)(v >> 32));
+        return ((uint64_t)hi << 32) | lo;
+    } else {
+        return __shfl_xor(v, M);
+    }
+}
+
+// One bitonic stage: blocks of 2^S elements, compare distance 2^T.  A block sorts
+// descending when bit S of its element index is 0 (the 512-block always); bit S >= 3
+// of the index 8*lane + e is lane bit S - 3.
+template <int S, int T>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&x)[8], int lane) {
+    const bool desc_lane = S == 9 || ((lane >> (S >= 3 ? S - 3 : 0)) & 1) == 0;
+    if constexpr (T >= 3) {
+        constexpr int M = 1 << (T - 3);
+        // the lane with the lower index keeps the larger key in a descending block
+        const bool keep_max = ((lane & M) == 0) == desc_lane;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint64_t p = xor_lane64<M>(x[e]);
+            x[e] = (x[e] > p) == keep_max ? x[e] : p;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (e & (1 << T)) continue;
+            const int e2 = e | (1 << T);
+            const bool desc = S >= 3 ? desc_lane : ((e >> S) & 1) == 0;
+            const bool swap = (x[e] > x[e2]) != desc;
+            const uint64_t a = x[e], b = x[e2];
+            x[e] = swap ? b : a;
+            x[e2] = swap ? a : b;
+        }
+    }
+}
+
+template <int S, int T>
+__device__ __forceinline__ void bitonic_merge_steps(uint64_t (&x)[8], int lane) {
+    bitonic_stage<S, T>(x, lane);
+    if constexpr (T > 0) bitonic_merge_steps<S, T - 1>(x, lane);
+}
+
+template <int S>
+__device__ __forceinline__ void bitonic_blocks(uint64_t (&x)[8], int lane) {
+    bitonic_merge_steps<S, S - 1>(x, lane);
+    if constexpr (S < 9) bitonic_blocks<S + 1>(x, lane);
+}
+
+// Sorts the 512 keys x (element 8*lane + e in x[e]) into descending order.
+__device__ __forceinline__ void sort512_desc(uint64_t (&x)[8]) {
+    bitonic_blocks<1>(x, lane_id());
+}
+
+__global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A) {
+    const int lane = lane_id();
+    const int64_t nrows = A.chunk_row1 - A.chunk_row0;
+    const int64_t id = (int64_t)blockIdx.x * kSortWaves + wave_id();
+    if (id >= A.B * nrows) return;
+    const int64_t b = id / nrows;
+    const int64_t r = id - b * nrows;
+    const int64_t row = A.chunk_row0 + r;
+    const int64_t slot0 = (b * A.QC + r) * A.P_ws;
+    const int64_t n_t = visible_keys(A.q_pos0 + row, A.m, A.T);
+    // the clamp keeps a corrupted count inside the list
+    const int n = n_t > 0 ? min(max(A.cnt[slot0], 0), A.k) : 0;
+
+    // slots 8*lane .. 8*lane+7 of the list (all inside it: its stride is above 512)
+    const uint64_t* src = A.cand + slot0 * (int64_t)A.CG + 8 * lane;
+    uint64_t x[8];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + e);
+        x[e] = ((uint64_t)v.y << 32) | v.x;
+        x[e + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 8 * lane + e < n ? x[e] : 0ull;
+    sort512_desc(x);
+
+    int32_t* oi = A.out_idx + (b * A.S + row) * (int64_t)A.k + 8 * lane;
+    float* os = A.out_score + (b * A.S + row) * (int64_t)A.k + 8 * lane;
+    int32_t vi[8];
+    float vs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bool real = 8 * lane + e < n;
+        vi[e] = real ? key_index(x[e]) : -1;
+        vs[e] = real ? key_score(x[e]) : -__builtin_inff();
+    }
+    if (8 * lane + 8 <= A.k && (A.k & 3) == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+            *reinterpret_cast<u32x4*>(oi + e) = u32x4{(uint32_t)vi[e], (uint32_t)vi[e + 1],
+                                                      (uint32_t)vi[e + 2], (uint32_t)vi[e + 3]};
+            *reinterpret_cast<u32x4*>(os + e) =
+                u32x4{__float_as_uint(vs[e]), __float_as_uint(vs[e + 1]),
+                      __float_as_uint(vs[e + 2]), __float_as_uint(vs[e + 3])};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (8 * lane + e < A.k) {
+                oi[e] = vi[e];
+                os[e] = vs[e];
+            }
+        }
+    }
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-    const int64_t grid = a.B * (a.chunk_row1 - a.chunk_row0);
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(64),
+    const int64_t rows = a.B * (a.chunk_row1 - a.chunk_row0);
+    if (rows <= 0) return hipSuccess;
+    if (a.P_chunk == 1 && a.k <= kSortN && a.CG >= kSortN) {
+        const int64_t grid = (rows + kSortWaves - 1) / kSortWaves;
+        hipLaunchKernelGGL(merge_sort_kernel, dim3((unsigned)grid), dim3(kSortWaves * 64), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(64),
                        (size_t)a.lds_entries * sizeof(uint64_t), stream, a);
     return hipGetLastError();
 }
