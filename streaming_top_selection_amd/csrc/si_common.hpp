@@ -43,8 +43,9 @@ __device__ __forceinline__ int mfma_row(int r, int lane) {
 // among equal scores the lower index has the larger key.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ord_f32(float x) {
-    uint32_t u = __float_as_uint(x);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    // negative: all bits flipped; otherwise the sign bit set
+    const uint32_t u = __float_as_uint(x);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float unord_f32(uint32_t o) {

@@ -123,15 +123,26 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
     int my_base = 0;
     if (lane < kTQ && my_count > 0) my_base = atomicAdd(&sCnt[lane], my_count);
     // pass 2: write each (register, block) as one run per half; every lane stores
-    // (lanes with no survivor into the list's pad slots), so no store needs a branch
+    // (lanes with no survivor into the list's pad slots), so no store needs a branch.
+    // A lane keeps its row's next free position in a register: its rank among its
+    // half's survivors is its rank in the whole wave, less (upper half) the lower
+    // half's survivors.  Per-half choices are bit selects on `half` (all ones in the
+    // upper half), and the compares are redone on an opaque copy of the thresholds,
+    // so no per-(register, block) mask has to survive from pass 1 in scalar registers.
+    uint32_t half = upper ? ~0u : 0u;
+    asm volatile("" : "+v"(half));
+    auto sel = [&](uint32_t hi, uint32_t lo) { return (half & hi) | (~half & lo); };
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(thf[r]));
     uint32_t low[KB];                       // key low bits: ~index
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) low[kb] = ~(uint32_t)(kbase + kb * kMB + il);
+    const uint32_t pad = (uint32_t)CG | (uint32_t)il;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int q_lo = mfma_row(r, 0), q_hi = mfma_row(r, 32);
-        int b_lo = __builtin_amdgcn_readlane(my_base, q_lo);
-        int b_hi = __builtin_amdgcn_readlane(my_base, q_hi);
+        uint32_t next = sel((uint32_t)__builtin_amdgcn_readlane(my_base, q_hi),
+                            (uint32_t)__builtin_amdgcn_readlane(my_base, q_lo));
         uint64_t* const row = cand_tile + (int64_t)(upper ? q_hi : q_lo) * row_stride;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -139,16 +150,14 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
             const uint64_t m = __ballot(pass);
             if (m == 0ull) continue;
             const uint32_t m_lo = (uint32_t)m, m_hi = (uint32_t)(m >> 32);
-            // survivors below this lane in its half
-            const int below = (int)__builtin_amdgcn_mbcnt_hi(
-                m_hi, upper ? 0u : __builtin_amdgcn_mbcnt_lo(m_lo, 0u));
-            const int at = (upper ? b_hi : b_lo) + below;
-            // the compaction policy keeps every position below CG; the bound only keeps
-            // a broken invariant from writing outside this query's list
-            const int dst = pass && at < CG ? at : CG + il;
+            const uint32_t n_lo = (uint32_t)__popc(m_lo), n_hi = (uint32_t)__popc(m_hi);
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u)) -
+                                  (half & n_lo);
+            // the compaction policy keeps every position below CG; the clamp only
+            // keeps a broken invariant inside this query's pad slots
+            const uint32_t dst = min(pass ? next + rank : ~0u, pad);
             row[dst] = ((uint64_t)ord_f32(acc[kb][r]) << 32) | low[kb];
-            b_lo += __popc(m_lo);
-            b_hi += __popc(m_hi);
+            next += sel(n_hi, n_lo);
         }
     }
 }
