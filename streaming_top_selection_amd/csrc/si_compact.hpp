@@ -63,12 +63,15 @@ __device__ __forceinline__ int hist_find(const uint32_t* hist, int rank, uint32_
 
 // The rank_in_bin-th largest (1-based) of the valid keys in score bin d1, when that
 // bin holds at most 64 keys: gathered one per lane through `stage` (64 u64 of LDS
-// owned by the wave) and ranked by counting the larger ones.
+// owned by the wave, 16-byte aligned) and ranked by counting the larger ones.  The
+// slots past the bin's keys hold 0, below every key, so every lane compares against
+// all 64 slots with no bound: 32 broadcast 16-byte reads and no wait per key.
 template <int E>
 __device__ __forceinline__ uint64_t select_small_bin(const uint64_t (&v)[E], int cnt,
                                                      const uint32_t (&bins)[E], int d1,
                                                      int rank_in_bin, uint64_t* stage) {
     const int lane = lane_id();
+    stage[lane] = 0ull;   // LDS operations of one wave complete in order
     int n = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -80,9 +83,13 @@ __device__ __forceinline__ uint64_t select_small_bin(const uint64_t (&v)[E], int
         n += __popcll(m);
     }
     wave_sync();
-    const uint64_t mine = lane < n ? stage[lane] : 0ull;
+    const uint64_t mine = stage[lane];
     int greater = 0;
-    for (int j = 0; j < n; ++j) greater += stage[j] > mine ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < 64; j += 2) {
+        const u64x2 p = *reinterpret_cast<const u64x2*>(&stage[j]);
+        greater += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);
+    }
     const uint64_t hit = __ballot(lane < n && greater == rank_in_bin - 1);
     const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
     wave_sync();

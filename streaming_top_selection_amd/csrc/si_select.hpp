@@ -178,7 +178,7 @@ select_kernel(SelectArgs A) {
     __shared__ int32_t sCnt[kTQ];          // candidates in the query's buffer
     __shared__ int32_t sN[kTQ];            // end of the query's visible keys here
     __shared__ uint32_t sHist[NWAVE][256];
-    __shared__ uint64_t sStage[NWAVE][64];
+    __shared__ __attribute__((aligned(16))) uint64_t sStage[NWAVE][64];
 
     const Problem& P = A.P;
     const int tid = threadIdx.x;
