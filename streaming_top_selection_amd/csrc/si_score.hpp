@@ -20,8 +20,8 @@
 //  * Software pipeline: the MFMAs of the next block are issued interleaved with the
 //    VALU epilogue (ReLU, weighted sum) of the current one, so both pipes stay busy
 //    in each wave; the LDS reads of head h+1 and the loads of head h+7 are issued in
-//    the shadow of step h's MFMAs, so only the barrier sits between the last MFMA of
-//    a step and the first of the next.
+//    the shadow of step h's MFMAs, so at most a barrier (one per two heads) sits
+//    between the last MFMA of a step and the first of the next.
 //  * Output layout: queries are MFMA rows and keys columns, so lane l owns key
 //    (l & 31) of each block and query rows mfma_row(r, l).  A query's scores for
 //    32 consecutive keys sit in one register across 32 lanes, which lets the
@@ -260,10 +260,12 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     //
     // Step h (buffers known at compile time): read head h+1 from buffer (h+1) % 8;
     // for kb = 0..KB-1 run the MFMAs of block (h, kb) + ZR - 1 beside the epilogue of
-    // (h, kb); load head h+7 into buffer (h+7) % 8 (last read in step h-1); publish
-    // head h+2.  Heads run in groups of 8; steps past H-1 see zero head weights (their
-    // epilogue adds exact zeros) and re-loaded data of head H-1, so the arithmetic of
-    // every real head is the same for any H.
+    // (h, kb); load head h+7 into buffer (h+7) % 8 (last read in step h-2, before the
+    // previous barrier).  Barriers come after odd steps only: the one after step h
+    // publishes heads h+2 and h+3, read in the next two steps.  Heads run in groups of
+    // 8; steps past H-1 see zero head weights (their epilogue adds exact zeros) and
+    // re-loaded data of head H-1, so the arithmetic of every real head is the same for
+    // any H.
     constexpr int ZR = (KB == 1) ? 2 : ((KB % 3 == 0) ? 3 : 2);   // accumulator slots
     constexpr int LA = ZR - 1;                                     // blocks of lookahead
     static_assert((kQBuf * KB) % ZR == 0, "slots must repeat every group of 8 heads");
@@ -298,10 +300,13 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
             interleave(kb, nread);
             pin(acc[kb]);
         }
-        // head h+2 (read in step h+1) must have landed: every wave issues QN loads
-        // per head, so <= (AHEAD-1)*QN younger loads means it has
-        SI_WAIT_VMCNT((AHEAD - 1) * QN);
-        loop_barrier();
+        // after an odd step h, heads h+2 and h+3 (read in steps h+1, h+2) must have
+        // landed: every wave issues QN loads per head, so <= (AHEAD-2)*QN younger
+        // loads means they have
+        if constexpr (R % 2 == 1) {
+            SI_WAIT_VMCNT((AHEAD - 2) * QN);
+            loop_barrier();
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -313,7 +318,7 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     using I7 = std::integral_constant<int, 7>;
     static_assert(kQBuf == 8 && AHEAD == 6, "the unrolled loop below assumes 8 buffers");
 
-    // prologue: heads 0..6 in flight into buffers 0..6, heads 0 and 1 published
+    // prologue: heads 0..6 in flight into buffers 0..6, heads 0, 1 and 2 published
     qload(Q.p[0], 0);
     qload(Q.p[1], 1);
     qload(Q.p[2], 2);
@@ -321,7 +326,7 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     qload(Q.p[4], 4);
     qload(Q.p[5], 5);
     qload(Q.p[6], 6);
-    SI_WAIT_VMCNT((AHEAD - 1) * QN);
+    SI_WAIT_VMCNT((AHEAD - 2) * QN);
     loop_barrier();
     qread(Q.p[0], bq[0], 0, 8);
     wread(0, wv[0]);
