@@ -286,7 +286,10 @@ def main(argv=None):
             "flops_per_step": flops,
         },
         "merge": {
-            "kernel": "merge_kernel", "bound": "hbm", "achieved": merge_gbps,
+            "kernel": ("merge_sort_kernel (one list per row, register bitonic sort)"
+                       if pl.n_partitions == 1 and spec.k <= 512
+                       else "merge_kernel (LDS gather, select, bitonic sort)"),
+            "bound": "hbm", "achieved": merge_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": merge_gbps / HBM_PEAK_GBPS,
             "mean_launch_ms": mrg_mean_s * 1e3, "bytes_per_step": merge_bytes,
         },
