@@ -111,10 +111,11 @@ def test_ragged_every_row(gpu_lib, q_pos0):
                       oa["w"], spec.m, q_pos0=q_pos0, b=1)
 
 
-@pytest.mark.parametrize("H,S,key_tile", [(3, 300, 512), (5, 1100, 512), (13, 700, 64)])
+@pytest.mark.parametrize("H,S,key_tile", [(3, 300, 512), (5, 1100, 512), (13, 700, 64),
+                                          (128, 700, 512)])
 def test_odd_heads_and_ratio(gpu_lib, H, S, key_tile):
-    """Head counts that are not a multiple of 8, m = 1 (every earlier key visible), and
-    rows whose keys span several register tiles (the q pipeline carried across tiles)."""
+    """Head counts that are not a multiple of 8 and the largest supported (128), m = 1
+    (every earlier key visible), and rows whose keys span several register tiles."""
     spec = synth.InputSpec(B=1, S=S, T=S, H=H, m=1, k=100, seed=22 + H)
     say("odd heads", H, S, key_tile)
     xc = synth.make_inputs(spec)
