@@ -13,17 +13,19 @@
 //            range, and each register writes its survivors as contiguous runs;
 // and after every key_tile keys (NSUB register tiles):
 //   compact  a query whose buffer could overflow in the next key tile is reduced, by
-//            one wave, to its exact top-k (wave radix select over the 64-bit keys held
-//            in registers); the k-th key's score becomes the threshold.
-// At the end of the partition each buffer is compacted to at most k entries; the
-// merge stage sorts and merges the partition lists.
+//            one wave with the keys in registers, to its best keys: between k and a
+//            little more than k mid-partition (whole score bins, see si_compact.hpp),
+//            exactly k at the partition's end; the smallest kept key's score becomes
+//            the threshold.
+// The merge stage then sorts (one partition) or merges the partition lists.
 //
-// Correctness of the threshold: after a compaction the buffer holds the k best keys
-// seen so far and the threshold key theta is the k-th of them; a later key below theta
-// has k better keys already and can never enter the top-k.  Keys are unique (score
-// bits, ~index).  Every key compared with theta comes from a later register tile, so
-// its index is larger than theta's and a score equal to theta's loses the tie: the
-// exact test "key > theta" is the float compare "score > score(theta)".
+// Correctness of the threshold: after a compaction the buffer holds the best keys
+// seen so far, at least k of them, and the threshold key theta is the smallest kept
+// one; a later key below theta has k better keys already and can never enter the
+// top-k.  Keys are unique (score bits, ~index).  Every key compared with theta comes
+// from a later register tile, so its index is larger than theta's and a score equal
+// to theta's loses the tie: the exact test "key > theta" is the float compare
+// "score > score(theta)".
 #pragma once
 
 #include "si_compact.hpp"
