@@ -125,7 +125,10 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
     int my_base = 0;
     if (lane < kTQ && my_count > 0) my_base = atomicAdd(&sCnt[lane], my_count);
     // pass 2: write each (register, block) as one run per half; every lane stores
-    // (lanes with no survivor into the list's pad slots), so no store needs a branch.
+    // (lanes with no survivor into the list's pad slots), so no store needs a branch,
+    // and a group with no survivor at all is not skipped either: with no branch the
+    // 16 x KB groups form one block the compiler can overlap (the pass is latency-bound
+    // at one wave per SIMD).
     // A lane keeps its row's next free position in a register: its rank among its
     // half's survivors is its rank in the whole wave, less (upper half) the lower
     // half's survivors.  Per-half choices are bit selects on `half` (all ones in the
@@ -150,7 +153,6 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
         for (int kb = 0; kb < KB; ++kb) {
             const bool pass = passes(r, kb);
             const uint64_t m = __ballot(pass);
-            if (m == 0ull) continue;
             const uint32_t m_lo = (uint32_t)m, m_hi = (uint32_t)(m >> 32);
             const uint32_t n_lo = (uint32_t)__popc(m_lo), n_hi = (uint32_t)__popc(m_hi);
             const uint32_t rank = __builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u)) -
