@@ -94,10 +94,10 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeArgs A) {
 // ---- one partition per row and k <= 512: a register sort -----------------------
 // The row's single list already holds its top-k (the select stage compacted it to at
 // most k keys), so the merge is a sort.  One wave per row; lane l holds elements
-// 8l .. 8l+7 of a 512-key bitonic network (padding keys are 0, below every real
-// key), so strides 1, 2, 4 compare within a lane and strides 8 .. 256 against lane
-// l ^ (stride / 8).  Loads and stores are contiguous 64-byte runs per lane.
-constexpr int kSortN = 512;
+// EPL*l .. EPL*l + EPL-1 of a 64*EPL-key bitonic network (EPL = 8, 16 or 32 keys per
+// lane for k up to 512, 1024, 2048; padding keys are 0, below every real key), so
+// strides below EPL compare within a lane and strides EPL .. 32*EPL against lane
+// l ^ (stride / EPL).  Loads and stores are contiguous runs per lane.
 constexpr int kSortWaves = 4;
 
 // 64-bit lane exchange: partner lane ^ m (DPP within a quad for m = 1, 2)
@@ -112,27 +112,28 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
     }
 }
 
-// One bitonic stage: blocks of 2^S elements, compare distance 2^T.  A block sorts
-// descending when bit S of its element index is 0 (the 512-block always); bit S >= 3
-// of the index 8*lane + e is lane bit S - 3.
-template <int S, int T>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&x)[8], int lane) {
-    const bool desc_lane = S == 9 || ((lane >> (S >= 3 ? S - 3 : 0)) & 1) == 0;
-    if constexpr (T >= 3) {
-        constexpr int M = 1 << (T - 3);
+// One bitonic stage: blocks of 2^S elements, compare distance 2^T, LE = log2(EPL).
+// A block sorts descending when bit S of its element index is 0 (the whole network's
+// block always); bit S >= LE of the index EPL*lane + e is lane bit S - LE.
+template <int LE, int S, int T>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&x)[1 << LE], int lane) {
+    constexpr int EPL = 1 << LE, LN = LE + 6;   // log2 of the network size
+    const bool desc_lane = S == LN || ((lane >> (S >= LE ? S - LE : 0)) & 1) == 0;
+    if constexpr (T >= LE) {
+        constexpr int M = 1 << (T - LE);
         // the lane with the lower index keeps the larger key in a descending block
         const bool keep_max = ((lane & M) == 0) == desc_lane;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < EPL; ++e) {
             const uint64_t p = xor_lane64<M>(x[e]);
             x[e] = (x[e] > p) == keep_max ? x[e] : p;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < EPL; ++e) {
             if (e & (1 << T)) continue;
             const int e2 = e | (1 << T);
-            const bool desc = S >= 3 ? desc_lane : ((e >> S) & 1) == 0;
+            const bool desc = S >= LE ? desc_lane : ((e >> S) & 1) == 0;
             const bool swap = (x[e] > x[e2]) != desc;
             const uint64_t a = x[e], b = x[e2];
             x[e] = swap ? b : a;
@@ -141,24 +142,27 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&x)[8], int lane) {
     }
 }
 
-template <int S, int T>
-__device__ __forceinline__ void bitonic_merge_steps(uint64_t (&x)[8], int lane) {
-    bitonic_stage<S, T>(x, lane);
-    if constexpr (T > 0) bitonic_merge_steps<S, T - 1>(x, lane);
+template <int LE, int S, int T>
+__device__ __forceinline__ void bitonic_merge_steps(uint64_t (&x)[1 << LE], int lane) {
+    bitonic_stage<LE, S, T>(x, lane);
+    if constexpr (T > 0) bitonic_merge_steps<LE, S, T - 1>(x, lane);
 }
 
-template <int S>
-__device__ __forceinline__ void bitonic_blocks(uint64_t (&x)[8], int lane) {
-    bitonic_merge_steps<S, S - 1>(x, lane);
-    if constexpr (S < 9) bitonic_blocks<S + 1>(x, lane);
+template <int LE, int S>
+__device__ __forceinline__ void bitonic_blocks(uint64_t (&x)[1 << LE], int lane) {
+    bitonic_merge_steps<LE, S, S - 1>(x, lane);
+    if constexpr (S < LE + 6) bitonic_blocks<LE, S + 1>(x, lane);
 }
 
-// Sorts the 512 keys x (element 8*lane + e in x[e]) into descending order.
-__device__ __forceinline__ void sort512_desc(uint64_t (&x)[8]) {
-    bitonic_blocks<1>(x, lane_id());
+// Sorts the 64*EPL keys x (element EPL*lane + e in x[e]) into descending order.
+template <int LE>
+__device__ __forceinline__ void sort_desc(uint64_t (&x)[1 << LE]) {
+    bitonic_blocks<LE, 1>(x, lane_id());
 }
 
+template <int LE>
 __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A) {
+    constexpr int EPL = 1 << LE;
     const int lane = lane_id();
     const int64_t nrows = A.chunk_row1 - A.chunk_row0;
     const int64_t id = (int64_t)blockIdx.x * kSortWaves + wave_id();
@@ -171,57 +175,68 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A
     // the clamp keeps a corrupted count inside the list
     const int n = n_t > 0 ? min(max(A.cnt[slot0], 0), A.k) : 0;
 
-    // slots 8*lane .. 8*lane+7 of the list (all inside it: its stride is above 512)
-    const uint64_t* src = A.cand + slot0 * (int64_t)A.CG + 8 * lane;
-    uint64_t x[8];
+    // slots EPL*lane .. EPL*lane + EPL-1 of the list (all inside it: the launcher
+    // checks that its stride holds 64*EPL slots)
+    const uint64_t* src = A.cand + slot0 * (int64_t)A.CG + EPL * lane;
+    uint64_t x[EPL];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
+    for (int e = 0; e < EPL; e += 2) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + e);
         x[e] = ((uint64_t)v.y << 32) | v.x;
         x[e + 1] = ((uint64_t)v.w << 32) | v.z;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 8 * lane + e < n ? x[e] : 0ull;
-    sort512_desc(x);
+    for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < n ? x[e] : 0ull;
+    sort_desc<LE>(x);
 
-    int32_t* oi = A.out_idx + (b * A.S + row) * (int64_t)A.k + 8 * lane;
-    float* os = A.out_score + (b * A.S + row) * (int64_t)A.k + 8 * lane;
-    int32_t vi[8];
-    float vs[8];
+    int32_t* oi = A.out_idx + (b * A.S + row) * (int64_t)A.k + EPL * lane;
+    float* os = A.out_score + (b * A.S + row) * (int64_t)A.k + EPL * lane;
+    if (EPL * lane + EPL <= A.k && (A.k & 3) == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const bool real = 8 * lane + e < n;
-        vi[e] = real ? key_index(x[e]) : -1;
-        vs[e] = real ? key_score(x[e]) : -__builtin_inff();
-    }
-    if (8 * lane + 8 <= A.k && (A.k & 3) == 0) {
+        for (int e = 0; e < EPL; e += 4) {
+            int32_t vi[4];
+            float vs[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 4) {
-            *reinterpret_cast<u32x4*>(oi + e) = u32x4{(uint32_t)vi[e], (uint32_t)vi[e + 1],
-                                                      (uint32_t)vi[e + 2], (uint32_t)vi[e + 3]};
+            for (int j = 0; j < 4; ++j) {
+                const bool real = EPL * lane + e + j < n;
+                vi[j] = real ? key_index(x[e + j]) : -1;
+                vs[j] = real ? key_score(x[e + j]) : -__builtin_inff();
+            }
+            *reinterpret_cast<u32x4*>(oi + e) =
+                u32x4{(uint32_t)vi[0], (uint32_t)vi[1], (uint32_t)vi[2], (uint32_t)vi[3]};
             *reinterpret_cast<u32x4*>(os + e) =
-                u32x4{__float_as_uint(vs[e]), __float_as_uint(vs[e + 1]),
-                      __float_as_uint(vs[e + 2]), __float_as_uint(vs[e + 3])};
+                u32x4{__float_as_uint(vs[0]), __float_as_uint(vs[1]), __float_as_uint(vs[2]),
+                      __float_as_uint(vs[3])};
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (8 * lane + e < A.k) {
-                oi[e] = vi[e];
-                os[e] = vs[e];
+        for (int e = 0; e < EPL; ++e) {
+            if (EPL * lane + e < A.k) {
+                const bool real = EPL * lane + e < n;
+                oi[e] = real ? key_index(x[e]) : -1;
+                os[e] = real ? key_score(x[e]) : -__builtin_inff();
             }
         }
     }
 }
 
+template <int LE>
+static hipError_t launch_merge_sort(const MergeArgs& a, int64_t rows, hipStream_t stream) {
+    const int64_t grid = (rows + kSortWaves - 1) / kSortWaves;
+    hipLaunchKernelGGL(merge_sort_kernel<LE>, dim3((unsigned)grid), dim3(kSortWaves * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     const int64_t rows = a.B * (a.chunk_row1 - a.chunk_row0);
     if (rows <= 0) return hipSuccess;
-    if (a.P_chunk == 1 && a.k <= kSortN && a.CG >= kSortN) {
-        const int64_t grid = (rows + kSortWaves - 1) / kSortWaves;
-        hipLaunchKernelGGL(merge_sort_kernel, dim3((unsigned)grid), dim3(kSortWaves * 64), 0,
-                           stream, a);
-        return hipGetLastError();
+    // one partition: sort the single list in registers (the list stride must hold the
+    // network's 64*EPL slots, which every planned capacity does)
+    if (a.P_chunk == 1) {
+        if (a.k <= 512 && a.CG >= 512) return launch_merge_sort<3>(a, rows, stream);
+        if (a.k <= 1024 && a.CG >= 1024) return launch_merge_sort<4>(a, rows, stream);
+        if (a.k <= 2048 && a.CG >= 2048) return launch_merge_sort<5>(a, rows, stream);
     }
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(64),
                        (size_t)a.lds_entries * sizeof(uint64_t), stream, a);
