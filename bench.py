@@ -287,7 +287,7 @@ def main(argv=None):
         },
         "merge": {
             "kernel": ("merge_sort_kernel (one list per row, register bitonic sort)"
-                       if pl.n_partitions == 1 and spec.k <= 512
+                       if pl.n_partitions == 1 and spec.k <= 2048
                        else "merge_kernel (LDS gather, select, bitonic sort)"),
             "bound": "hbm", "achieved": merge_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": merge_gbps / HBM_PEAK_GBPS,
