@@ -354,6 +354,11 @@ def summarize(root):
     print(f"select_kernel FETCH_SIZE {sel} KiB, WRITE_SIZE {wr} KiB per launch")
     print(f"copy probe ({COPY_PROBE_BYTES} B read + written): FETCH_SIZE {cf} KiB, "
           f"WRITE_SIZE {cw} KiB -> scale fetch x{fetch_scale}, write x{write_scale}")
+    mf = _pmc_value(os.path.join(root, "fetch"), "FETCH_SIZE", "merge")
+    mw = _pmc_value(os.path.join(root, "write"), "WRITE_SIZE", "merge")
+    if mf is not None and mw is not None and fetch_scale and write_scale:
+        print(f"merge FETCH_SIZE {mf} KiB, WRITE_SIZE {mw} KiB per launch -> "
+              f"{mf * 1024 * fetch_scale:.0f} B read, {mw * 1024 * write_scale:.0f} B written")
     if fetch_b is not None and write_b is not None:
         rec = {"kernel_source_sha256_16": kernel_source_hash(),
                "fetch_bytes": fetch_b, "write_bytes": write_b,
