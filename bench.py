@@ -148,8 +148,8 @@ def main(argv=None):
         return summarize(args.dir)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(query rows shard across GPUs with no exchange; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(query rows would shard across GPUs with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
