@@ -160,35 +160,12 @@ __device__ __forceinline__ void sort_desc(uint64_t (&x)[1 << LE]) {
     bitonic_blocks<LE, 1>(x, lane_id());
 }
 
+// Writes row `row` of batch entry b: the first n (<= k) of the sorted keys x (element
+// EPL*lane + e in x[e]) as (index, score), then -1 / -inf up to k.
 template <int LE>
-__global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A) {
+__device__ __forceinline__ void write_sorted_row(const MergeArgs& A, int64_t b, int64_t row,
+                                                 const uint64_t (&x)[1 << LE], int n, int lane) {
     constexpr int EPL = 1 << LE;
-    const int lane = lane_id();
-    const int64_t nrows = A.chunk_row1 - A.chunk_row0;
-    const int64_t id = (int64_t)blockIdx.x * kSortWaves + wave_id();
-    if (id >= A.B * nrows) return;
-    const int64_t b = id / nrows;
-    const int64_t r = id - b * nrows;
-    const int64_t row = A.chunk_row0 + r;
-    const int64_t slot0 = (b * A.QC + r) * A.P_ws;
-    const int64_t n_t = visible_keys(A.q_pos0 + row, A.m, A.T);
-    // the clamp keeps a corrupted count inside the list
-    const int n = n_t > 0 ? min(max(A.cnt[slot0], 0), A.k) : 0;
-
-    // slots EPL*lane .. EPL*lane + EPL-1 of the list (all inside it: the launcher
-    // checks that its stride holds 64*EPL slots)
-    const uint64_t* src = A.cand + slot0 * (int64_t)A.CG + EPL * lane;
-    uint64_t x[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; e += 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + e);
-        x[e] = ((uint64_t)v.y << 32) | v.x;
-        x[e + 1] = ((uint64_t)v.w << 32) | v.z;
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < n ? x[e] : 0ull;
-    sort_desc<LE>(x);
-
     int32_t* oi = A.out_idx + (b * A.S + row) * (int64_t)A.k + EPL * lane;
     float* os = A.out_score + (b * A.S + row) * (int64_t)A.k + EPL * lane;
     if (EPL * lane + EPL <= A.k && (A.k & 3) == 0) {
@@ -221,6 +198,78 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A
 }
 
 template <int LE>
+__global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A) {
+    constexpr int EPL = 1 << LE;
+    const int lane = lane_id();
+    const int64_t nrows = A.chunk_row1 - A.chunk_row0;
+    const int64_t id = (int64_t)blockIdx.x * kSortWaves + wave_id();
+    if (id >= A.B * nrows) return;
+    const int64_t b = id / nrows;
+    const int64_t r = id - b * nrows;
+    const int64_t row = A.chunk_row0 + r;
+    const int64_t slot0 = (b * A.QC + r) * A.P_ws;
+    const int64_t n_t = visible_keys(A.q_pos0 + row, A.m, A.T);
+    // the clamp keeps a corrupted count inside the list
+    const int n = n_t > 0 ? min(max(A.cnt[slot0], 0), A.k) : 0;
+
+    // slots EPL*lane .. EPL*lane + EPL-1 of the list (all inside it: the launcher
+    // checks that its stride holds 64*EPL slots)
+    const uint64_t* src = A.cand + slot0 * (int64_t)A.CG + EPL * lane;
+    uint64_t x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + e);
+        x[e] = ((uint64_t)v.y << 32) | v.x;
+        x[e + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < n ? x[e] : 0ull;
+    sort_desc<LE>(x);
+
+    write_sorted_row<LE>(A, b, row, x, n, lane);
+}
+
+// Several partitions whose lists hold at most 64*EPL keys together: gathered into LDS
+// (one 64-lane group per row, as in merge_kernel), then sorted in registers; the
+// first min(k, total) keys are the row's top-k.
+template <int LE>
+__global__ void __launch_bounds__(64) merge_gather_sort_kernel(MergeArgs A) {
+    constexpr int EPL = 1 << LE;
+    __shared__ uint64_t sbuf[64 * EPL];
+    const int lane = lane_id();
+    const int64_t nrows = A.chunk_row1 - A.chunk_row0;
+    const int64_t b = (int64_t)blockIdx.x / nrows;
+    const int64_t r = (int64_t)blockIdx.x - b * nrows;
+    const int64_t row = A.chunk_row0 + r;
+    const int64_t n_t = visible_keys(A.q_pos0 + row, A.m, A.T);
+    const int Pt = n_t > 0 ? (int)min((int64_t)A.P_chunk, (n_t + A.KP - 1) / A.KP) : 0;
+    const int64_t slot0 = (b * A.QC + r) * A.P_ws;
+    // the clamps keep a corrupted count inside the lists and the buffer (the launcher
+    // checks partitions * k <= 64*EPL)
+    const int c = lane < Pt ? min(max(A.cnt[slot0 + lane], 0), A.k) : 0;
+    const int off = wave_excl_scan(c);
+    const int total = min(wave_sum(c), 64 * EPL);
+    for (int p = 0; p < Pt; ++p) {
+        const int cp = __shfl(c, p);
+        const int op = __shfl(off, p);
+        const uint64_t* src = A.cand + (slot0 + p) * (int64_t)A.CG;
+        for (int i = lane; i < cp && op + i < 64 * EPL; i += 64) sbuf[op + i] = src[i];
+    }
+    wave_sync();
+    uint64_t x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < total ? sbuf[EPL * lane + e] : 0ull;
+    sort_desc<LE>(x);
+    write_sorted_row<LE>(A, b, row, x, min(total, A.k), lane);
+}
+
+template <int LE>
+static hipError_t launch_merge_gather_sort(const MergeArgs& a, int64_t rows, hipStream_t stream) {
+    hipLaunchKernelGGL(merge_gather_sort_kernel<LE>, dim3((unsigned)rows), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int LE>
 static hipError_t launch_merge_sort(const MergeArgs& a, int64_t rows, hipStream_t stream) {
     const int64_t grid = (rows + kSortWaves - 1) / kSortWaves;
     hipLaunchKernelGGL(merge_sort_kernel<LE>, dim3((unsigned)grid), dim3(kSortWaves * 64), 0,
@@ -238,6 +287,11 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
         if (a.k <= 1024 && a.CG >= 1024) return launch_merge_sort<4>(a, rows, stream);
         if (a.k <= 2048 && a.CG >= 2048) return launch_merge_sort<5>(a, rows, stream);
     }
+    // several partitions holding at most 2048 keys together: gather, register sort
+    const int64_t entries = (int64_t)a.P_chunk * a.k;
+    if (entries <= 512) return launch_merge_gather_sort<3>(a, rows, stream);
+    if (entries <= 1024) return launch_merge_gather_sort<4>(a, rows, stream);
+    if (entries <= 2048) return launch_merge_gather_sort<5>(a, rows, stream);
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(64),
                        (size_t)a.lds_entries * sizeof(uint64_t), stream, a);
     return hipGetLastError();
