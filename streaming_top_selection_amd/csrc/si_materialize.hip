@@ -33,7 +33,7 @@ mat_score_kernel(MatScoreArgs A) {
     if (live) {
         load_w_tile<NWAVE * 64>(P, b, trow0, rows_valid, L);
         __syncthreads();
-        score_regs<NWAVE, KB, FP8>(P, b, trow0, rows_valid, key0, L, Q, acc);
+        score_regs<NWAVE, KB, FP8>(P, b, trow0, rows_valid, key0, P.T, L, Q, acc);
     }
     // register r holds row trow0 + mfma_row(r, lane); lanes run along the keys, so
     // each store writes 32 consecutive scores of two rows

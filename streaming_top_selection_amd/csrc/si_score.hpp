@@ -115,14 +115,15 @@ __device__ __forceinline__ void load_w_tile(const Problem& P, int64_t b, int64_t
 }
 
 // Scores rows [row0, row0 + rows_valid) against keys key0 + [0, NWAVE*KB*32).
-// Requires: L.w filled and a __syncthreads() since; key0 % 32 == 0; every thread of
-// the workgroup calls it.  acc[kb][r] receives the score of query row
-// row0 + mfma_row(r, lane) and key key0 + (wave*KB + kb)*32 + (lane & 31).  Keys >= T
-// score as if zero.
+// Requires: L.w filled and a __syncthreads() since; key0 % 32 == 0; key_end <= T;
+// every thread of the workgroup calls it.  acc[kb][r] receives the score of query row
+// row0 + mfma_row(r, lane) and key key0 + (wave*KB + kb)*32 + (lane & 31).  Keys >=
+// key_end score as if zero: a caller that masks them anyway passes the end of what any
+// of its rows sees, and zero operands there cost the MFMAs less power.
 template <int NWAVE, int KB, bool FP8>
 __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t row0,
-                                           int rows_valid, int64_t key0, ScoreLds& L,
-                                           const QBufs& Q, f32x16 (&acc)[KB]) {
+                                           int rows_valid, int64_t key0, int64_t key_end,
+                                           ScoreLds& L, const QBufs& Q, f32x16 (&acc)[KB]) {
     constexpr int NT = NWAVE * kWave;
     static_assert(kQBuf >= 4, "the pipeline reads head h+1 while loading h+kQBuf-1");
 
@@ -143,7 +144,7 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         const int64_t key = key0 + (int64_t)(wave * KB + kb) * kMB + il;
-        if (key < P.T) {
+        if (key < key_end) {
             if constexpr (!FP8) {
                 const u32x4* src = reinterpret_cast<const u32x4*>(
                     static_cast<const uint16_t*>(P.kc) + ((b * P.T + key) * kD + 64 * hh));

@@ -227,7 +227,7 @@ select_kernel(SelectArgs A) {
     int sub = 0;
     for (int64_t key0 = key_lo; key0 < key_hi; key0 += RT) {
         f32x16 acc[KB];
-        score_regs<NWAVE, KB, FP8>(P, b, row0, rows_valid, key0, L, Q, acc);
+        score_regs<NWAVE, KB, FP8>(P, b, row0, rows_valid, key0, key_hi, L, Q, acc);
 
         const int64_t kbase = key0 + (int64_t)wave * KB * kMB;
         uint64_t* const cand_tile = A.cand + slot0 * CGS;
