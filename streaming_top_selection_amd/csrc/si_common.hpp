@@ -70,30 +70,21 @@ __device__ __forceinline__ float key_score(uint64_t key) {
 __device__ __forceinline__ float canon_zero(float x) { return x + 0.0f; }
 
 // ---------------------------------------------------------------------------
-// OCP FP8 E4M3 byte -> bf16 bits.  Exact: every finite E4M3 value (3 mantissa
-// bits, exponents 2^-9 .. 2^8) is representable in bf16.
+// OCP FP8 E4M3 -> bf16.  Exact: every finite E4M3 value (3 mantissa bits, exponents
+// 2^-9 .. 2^8) is representable in bf16.  gfx950 converts two bytes per instruction
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1.0); an exhaustive check of all 256 codes in
+// each byte position against a field-by-field decode (sign, exponent rebias 7 -> 127,
+// subnormals normalised) matched for every finite code.  NaN codes are outside the
+// ABI contract.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t x) {
-    const uint32_t sign = (x & 0x80u) << 8;
-    const uint32_t e = (x >> 3) & 0xFu;
-    const uint32_t m = x & 0x7u;
-    uint32_t mag;
-    if (e != 0u) {
-        mag = ((e + 120u) << 7) | (m << 4);          // bias 7 -> bias 127
-    } else if (m == 0u) {
-        mag = 0u;
-    } else {                                          // subnormal m * 2^-9
-        const uint32_t p = 31u - __builtin_clz(m);    // 0..2
-        mag = ((p + 118u) << 7) | ((m << (7u - p)) & 0x7Fu);
-    }
-    return sign | mag;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// four E4M3 bytes (little-endian in a u32) -> four bf16 in two u32
+// four E4M3 bytes (little-endian in a u32) -> four bf16 in two u32 (byte 0 in the low
+// half of .x)
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
     u32x2 r;
-    r.x = e4m3_to_bf16_bits(w & 0xFFu) | (e4m3_to_bf16_bits((w >> 8) & 0xFFu) << 16);
-    r.y = e4m3_to_bf16_bits((w >> 16) & 0xFFu) | (e4m3_to_bf16_bits(w >> 24) << 16);
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     return r;
 }
 

@@ -149,6 +149,30 @@ def test_e4m3_keys_every_row(gpu_lib):
                       oa["w"], spec.m, kc_dtype="e4m3fn", kc_scale=oa["kc_scale"])
 
 
+def test_e4m3_every_code(gpu_lib):
+    """Keys holding every finite E4M3 code at every byte position of a word (d mod 4),
+    unit scales: the written scores against the oracle's own decoder, within beta,
+    and the streamed top-k of every row."""
+    spec = synth.InputSpec(B=1, S=256, T=256, H=4, m=1, k=32, seed=31, kc_dtype="e4m3fn")
+    say("e4m3 every code")
+    xc = synth.make_inputs(spec)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    s_idx = np.arange(spec.T)[:, None]
+    d_idx = np.arange(128)[None, :]
+    xc["kc"] = torch.from_numpy(codes[(s_idx + 7 * d_idx) % codes.size][None].copy())
+    xc["kc_scale"] = torch.ones((1, spec.T), dtype=torch.float32)
+    xd = dev(xc)
+    oa = oracle_args(xc, spec)
+    sc = gpu_lib.materialize_scores(xd["q"], xd["kc"], xd["w"], spec.m, kc_scale=xd["kc_scale"])
+    torch.cuda.synchronize()
+    check_score_block(sc[0].cpu().numpy(), range(spec.S), oa["q_bits"], oa["kc_bits"],
+                      oa["w"], spec.m, kc_dtype="e4m3fn", kc_scale=oa["kc_scale"])
+    gi, gs = run_stream(gpu_lib, xd, spec.m, spec.k)
+    check_rows(gi[0].cpu().numpy(), gs[0].cpu().numpy(), range(spec.S), oa["q_bits"],
+               oa["kc_bits"], oa["w"], spec.m, spec.k, kc_dtype="e4m3fn",
+               kc_scale=oa["kc_scale"])
+
+
 # ---------------------------------------------------------------------------
 # Knob invariance: no tuning knob changes an output bit
 # ---------------------------------------------------------------------------
