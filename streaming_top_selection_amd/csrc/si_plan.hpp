@@ -16,7 +16,7 @@ constexpr int32_t kPlanMaxK = 2048;
 constexpr int32_t kPlanD = 128;
 constexpr int32_t kMaxPartitions = 64;       // lists one merge wave gathers
 constexpr int64_t kMergeMaxEntries = 8192;   // 64 KiB of LDS keys in the merge
-constexpr int64_t kAutoWorkspaceCap = int64_t(3) << 29;   // 1.5 GiB: auto query_chunk bound
+constexpr int64_t kAutoWorkspaceCap = int64_t(3) << 30;   // 3 GiB: auto query_chunk bound
 constexpr int32_t kTargetGroups = 1024;      // workgroups one select launch aims for
 constexpr int32_t kPlanCandPad = 64;         // unread slots after each candidate list
 

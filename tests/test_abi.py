@@ -67,7 +67,7 @@ def test_plan_headline_workload_is_one_chunk_one_partition(lib):
 def test_plan_million_token_workspace_is_bounded():
     p = plan(S=1048576, T=262144, kc_dtype="e4m3fn")
     assert p.n_chunks * p.query_chunk >= 1048576
-    assert p.workspace_bytes <= (3 << 29) + 4096          # auto chunk keeps it <= 1.5 GiB
+    assert p.workspace_bytes <= (3 << 30) + 4096          # auto chunk keeps it <= 3 GiB
 
 
 def test_plan_small_problems_split_keys_into_partitions():
