@@ -38,8 +38,14 @@ WORKLOADS = {
                "fp32 w ~ N(0,1)/8, causal",
     "tiny": "Tiny indexer: B=1, S=1024, m=4, T=256, H_I=64, D=128, top-k=64",
     "small": "Small exactness check: B=2, S=8192, m=4, T=2048, H_I=64, D=128, top-k=512, 5% duplicate keys",
-    "long": "Long-context: B=1, S=262144, m=4, T=65536, H_I=64, D=128, top-k=512",
+    "long": "Long-context: B=1, S=262144, m=4, T=65536, H_I=64, D=128, top-k=512, bf16 q/k",
+    "million": "Million-token capacity: B=1, S=1048576, m=4, T=262144, H_I=64, D=128, top-k=512, "
+               "bf16 q, E4M3 keys with per-row fp32 scale",
 }
+# default (steps, warmup) per workload: about a minute of timed work at most
+DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1)}
+# q rows per slice of the million workload's streamed-q capacity pass
+CAPACITY_SLICE_ROWS = 16384
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +87,62 @@ def visible_pairs(S, T, m, q_pos0=0):
     return int(np.minimum(T, (t + 1) // m).sum())
 
 
+def cpu_model_name():
+    """The host CPU's model name (lscpu), or /proc/cpuinfo's, or "unknown"."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def tensor_bytes(*ts):
+    return int(sum(t.numel() * t.element_size() for t in ts if t is not None))
+
+
+def capacity_pass(si, spec, kc, kc_scale, w, dev, slice_rows=CAPACITY_SLICE_ROWS):
+    """The million-token run with q never resident whole: each slice of q rows is drawn,
+    scored at its absolute offset (q_pos0) into its rows of the outputs, then freed.
+    Returns (allocator peak over the pass, seconds of indexer calls, slices)."""
+    import torch
+
+    import synth
+    kc_dtype = "bf16" if kc_scale is None else "e4m3fn"
+    out = (torch.empty((spec.B, spec.S, spec.k), dtype=torch.int32, device=dev),
+           torch.empty((spec.B, spec.S, spec.k), dtype=torch.float32, device=dev))
+    # the widest slice is the last one: its plan sizes the shared workspace
+    pl = si.plan(spec.B, slice_rows, spec.T, spec.H, spec.D, spec.m, spec.k,
+                 q_pos0=spec.S - slice_rows, kc_dtype=kc_dtype)
+    ws = si.workspace(pl, dev)
+    stream = torch.cuda.current_stream(dev)
+    busy = 0.0
+    n = 0
+    for r0 in range(0, spec.S, slice_rows):
+        r1 = min(spec.S, r0 + slice_rows)
+        q = synth.gen_q_rows(spec, r0, r1, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        si.indexer_topk(q, kc, w[:, r0:r1], spec.m, spec.k, kc_scale=kc_scale, q_pos0=r0,
+                        out=(out[0][:, r0:r1], out[1][:, r0:r1]), ws=ws)
+        e1.record(stream)
+        e1.synchronize()
+        busy += e0.elapsed_time(e1) / 1e3
+        del q
+        n += 1
+    torch.cuda.synchronize(dev)
+    return torch.cuda.max_memory_allocated(dev), busy, n, out
+
+
 def cpu_baseline(spec, x, seconds, seed=100):
     """Time the float64 oracle on sampled query rows (roughly `seconds` of work)."""
     import numpy as np
@@ -95,6 +157,7 @@ def cpu_baseline(spec, x, seconds, seed=100):
                       default=1)
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    cpu_model = cpu_model_name()
     rows = synth.sample_rows(spec, 4096, salt=seed)
     rng = np.random.default_rng(seed)
     rng.shuffle(rows)
@@ -120,6 +183,7 @@ def cpu_baseline(spec, x, seconds, seed=100):
         "value": done_pairs / elapsed if elapsed > 0 else 0.0,
         "unit": "pairs/s",
         "cores": int(threads),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{len(done_rows)} query rows sampled uniformly over rows that see >= k keys "
                   f"(seed {seed}), float64 NumPy oracle, {done_pairs} visible pairs in "
@@ -130,8 +194,10 @@ def cpu_baseline(spec, x, seconds, seed=100):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 10; 5 for long, 3 for million)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 3; 1 for long and million)")
     ap.add_argument("--workload", default="v4flash", choices=sorted(WORKLOADS))
     ap.add_argument("--key-tile", type=int, default=0)
     ap.add_argument("--query-chunk", type=int, default=0)
@@ -143,9 +209,14 @@ def main(argv=None):
                     help="select-once / copy-probe: single launches for rocprofv3 counter "
                          "runs; summarize DIR: turn rocprofv3 CSV output into the summary")
     ap.add_argument("--dir", default=None, help="rocprofv3 output root for --mode summarize")
+    ap.add_argument("--timed-launches", type=int, default=5,
+                    help="--mode summarize: select launches of the profiled run's timed steps")
     args = ap.parse_args(argv)
+    d_steps, d_warm = DEFAULT_STEPS.get(args.workload, (10, 3))
+    args.steps = d_steps if args.steps is None else args.steps
+    args.warmup = d_warm if args.warmup is None else args.warmup
     if args.mode == "summarize":
-        return summarize(args.dir)
+        return summarize(args.dir, args.timed_launches, args.workload)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -161,9 +232,32 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     spec = synth.CONFIGS[args.workload]
+    capacity = None
+    if args.workload == "million" and args.mode == "bench":
+        # q streamed in slices, never resident whole: the peak HBM of the pages' capacity
+        # run (measured first, on an empty allocator, so nothing else inflates it)
+        kc0, ks0 = synth.gen_keys(spec, device=dev)
+        w0 = synth.gen_w_rows(spec, device=dev)
+        torch.cuda.synchronize(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        cap_peak, cap_s, cap_n, cap_out = capacity_pass(si, spec, kc0, ks0, w0, dev)
+        capacity = {"peak_hbm_bytes": int(cap_peak), "peak_hbm_gb": cap_peak / 1e9,
+                    "indexer_seconds": cap_s, "slices": cap_n, "slice_rows": CAPACITY_SLICE_ROWS,
+                    "pairs_per_s": spec.B * visible_pairs(spec.S, spec.T, spec.m) / cap_s}
+        del kc0, ks0, w0
+        torch.cuda.synchronize(dev)
+        torch.cuda.empty_cache()
+    x = synth.make_inputs(spec, device=dev)
+    torch.cuda.synchronize(dev)
+    if capacity is not None:
+        # the streamed run's outputs must equal the resident-q run's (checked below)
+        capacity_outputs = cap_out
+    # the peak of the timed work: inputs (already resident) + outputs + workspace; the
+    # generator's temporaries are behind this reset
+    torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats(dev)
     free0, total_mem = torch.cuda.mem_get_info(dev)
-    x = synth.make_inputs(spec, device=dev)
+    input_bytes = tensor_bytes(x["q"], x["kc"], x["kc_scale"], x["w"])
     kc_dtype = "bf16" if x["kc_scale"] is None else "e4m3fn"
     knobs = dict(key_tile=args.key_tile, query_chunk=args.query_chunk,
                  key_partition=args.key_partition)
@@ -171,6 +265,7 @@ def main(argv=None):
     ws = si.workspace(pl, dev)
     out = (torch.empty((spec.B, spec.S, spec.k), dtype=torch.int32, device=dev),
            torch.empty((spec.B, spec.S, spec.k), dtype=torch.float32, device=dev))
+    output_bytes = tensor_bytes(*out)
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
@@ -205,10 +300,20 @@ def main(argv=None):
 
     # the staged step is the product call: check once against si_indexer_topk itself
     step()
-    ref = si.indexer_topk(x["q"], x["kc"], x["w"], spec.m, spec.k, kc_scale=x["kc_scale"], **knobs)
+    ref = si.indexer_topk(x["q"], x["kc"], x["w"], spec.m, spec.k, kc_scale=x["kc_scale"],
+                          out=(torch.empty_like(out[0]), torch.empty_like(out[1])), ws=ws,
+                          **knobs)
     torch.cuda.synchronize(dev)
     assert torch.equal(ref[0], out[0]) and torch.equal(ref[1], out[1])
     del ref
+    if capacity is not None:
+        assert torch.equal(capacity_outputs[0], out[0]) and \
+            torch.equal(capacity_outputs[1], out[1]), "streamed-q run differs"
+        del capacity_outputs
+        capacity["equal_to_resident_run"] = True
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
 
     for _ in range(args.warmup):
         step()
@@ -272,6 +377,8 @@ def main(argv=None):
         "mfma_frac": achieved_tflops / BF16_DENSE_PEAK_TFLOPS,
         "peak_hbm_bytes": int(peak_alloc),
         "peak_hbm_gib": peak_alloc / 2 ** 30,
+        "hbm_bytes": {"inputs": input_bytes, "outputs": output_bytes,
+                      "workspace": int(ws.numel()), "allocator_peak_timed": int(peak_alloc)},
         "device_mem_delta_bytes": int(free0 - free1),
         "roofline": {
             "kernel": "select_kernel (fused bf16 MFMA scoring + running top-k)",
@@ -294,6 +401,8 @@ def main(argv=None):
             "mean_launch_ms": mrg_mean_s * 1e3, "bytes_per_step": merge_bytes,
         },
     }
+    if capacity is not None:
+        rec["streamed_q_capacity_run"] = capacity
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
         base, checked = cpu_baseline(spec, x, args.cpu_seconds)
         rec["cpu_baseline"] = base
@@ -332,10 +441,38 @@ def _kernel_stats(csv_dir):
     return rows
 
 
-def summarize(root):
+def _dispatches(csv_dir, kernel_substr):
+    """(dispatch id, duration ns) of every dispatch of a kernel in a kernel trace, in
+    dispatch order."""
+    import csv
+    out = []
+    for path in glob.glob(os.path.join(csv_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel_substr in r["Kernel_Name"]:
+                    out.append((int(r["Dispatch_Id"]),
+                                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return sorted(out)
+
+
+def timed_launch_stats(durations_ns, timed):
+    """Mean and median (us) of the last `timed` launches: the bench's timed steps come
+    last, after the equality check and the warm-up launches."""
+    import statistics
+    d = [x / 1e3 for x in durations_ns[-timed:]] if timed > 0 else []
+    if not d:
+        return None
+    return {"launches": len(d), "mean_us": statistics.fmean(d), "median_us": statistics.median(d)}
+
+
+def summarize(root, timed=5, workload="v4flash"):
     """Prints the markdown summary of a profile directory with subdirectories trace/
-    (kernel trace + stats), fetch/ and write/ (select-once counters) and copy_fetch/,
-    copy_write/ (copy-probe counters)."""
+    (kernel trace + stats of a bench run), clock/ (GRBM_GUI_ACTIVE + kernel trace of
+    select-once), fetch/ and write/ (select-once counters) and copy_fetch/, copy_write/
+    (copy-probe counters)."""
+    import synth
+    spec = synth.CONFIGS[workload]
+    flops = spec.B * visible_pairs(spec.S, spec.T, spec.m) * 2 * spec.H * spec.D
     stats = _kernel_stats(os.path.join(root, "trace"))
     sel = _pmc_value(os.path.join(root, "fetch"), "FETCH_SIZE", "select_kernel")
     wr = _pmc_value(os.path.join(root, "write"), "WRITE_SIZE", "select_kernel")
@@ -350,6 +487,25 @@ def summarize(root):
     for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
         print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['TotalDurationNs'])/1e6:.3f} | "
               f"{float(r['AverageNs'])/1e3:.1f} | {float(r['Percentage']):.2f} |")
+    print()
+    disp = _dispatches(os.path.join(root, "trace"), "select_kernel")
+    ts = timed_launch_stats([d for _, d in disp], timed)
+    if ts:
+        print(f"select_kernel, all {len(disp)} launches (us): "
+              f"{', '.join(f'{d / 1e3:.1f}' for _, d in disp)}")
+        print(f"select_kernel over the {ts['launches']} timed launches (the last ones): "
+              f"mean {ts['mean_us']:.1f} us, median {ts['median_us']:.1f} us")
+        frac = flops / (ts["mean_us"] * 1e-6) / (BF16_DENSE_PEAK_TFLOPS * 1e12)
+        print(f"roofline: {flops:.4e} algorithmic flop per launch / {ts['mean_us']:.1f} us = "
+              f"{flops / (ts['mean_us'] * 1e-6) / 1e12:.1f} TFLOP/s = {frac:.3f} of the "
+              f"{BF16_DENSE_PEAK_TFLOPS:.0f} TFLOP/s bf16 dense peak")
+    gg = _pmc_value(os.path.join(root, "clock"), "GRBM_GUI_ACTIVE", "select_kernel")
+    cd = _dispatches(os.path.join(root, "clock"), "select_kernel")
+    if gg and cd:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+        ghz = gg / 8 / cd[-1][1]
+        print(f"clock under the select kernel (GRBM_GUI_ACTIVE / 8 XCDs / duration of the "
+              f"same dispatch, {cd[-1][1] / 1e3:.1f} us): {ghz:.2f} GHz")
     print()
     print(f"select_kernel FETCH_SIZE {sel} KiB, WRITE_SIZE {wr} KiB per launch")
     print(f"copy probe ({COPY_PROBE_BYTES} B read + written): FETCH_SIZE {cf} KiB, "

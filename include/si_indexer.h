@@ -99,6 +99,20 @@ si_status si_indexer_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                           const si_config* cfg, si_plan* out);
 
 /*
+ * si_indexer_topk_workspace_bytes -- bytes of workspace si_indexer_topk needs for a
+ * problem whose first q row is absolute position 0 (q_pos0 = 0) with the knobs cfg
+ * (NULL = all automatic): the same value as si_indexer_plan(...).workspace_bytes.
+ * The workspace holds one query chunk's candidate lists, so its size is bounded by
+ * the chunk, not by S (chunked partition-merge: skillsdirectory.com "Streamindex Csa
+ * Topk", Implementation Steps 1-3).  A caller streaming q in slices with q_pos0 > 0
+ * uses si_indexer_plan, whose plan depends on q_pos0.  Host only.
+ * Returns SIZE_MAX when the arguments are invalid or not built (si_last_error()
+ * explains); 0 when there is nothing to do (B = 0 or S = 0).
+ */
+size_t si_indexer_topk_workspace_bytes(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
+                                       int32_t m, int32_t k, const si_config* cfg);
+
+/*
  * si_indexer_topk -- streaming top-k of the indexer scores (the hot path).
  *
  *  q         [B, S, H, D] bf16 query rows; row r is absolute position q_pos0 + r

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     materialize_topk,
     plan,
     workspace,
+    workspace_bytes,
 )
 from ._lib import SiError  # noqa: F401
 
@@ -22,5 +23,5 @@ _lib.load()
 
 __all__ = [
     "Plan", "SiError", "indexer_topk", "indexer_select_chunk", "indexer_merge_chunk",
-    "materialize_scores", "materialize_topk", "plan", "workspace",
+    "materialize_scores", "materialize_topk", "plan", "workspace", "workspace_bytes",
 ]

@@ -39,6 +39,7 @@ SIGNATURES = {
     "si_last_error": (ctypes.c_char_p, []),
     "si_indexer_plan": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _cfgp,
                                ctypes.POINTER(SiPlan)]),
+    "si_indexer_topk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _cfgp]),
     "si_indexer_topk": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,
                                _i32, _i64, _cfgp, _p, _p, _p, _sz, _p]),
     "si_indexer_select_chunk": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32,
@@ -60,7 +61,7 @@ def load():
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m streaming_top_selection_amd.build` "
+                f"{LIB_PATH} is missing: build it with `python streaming_top_selection_amd/build.py` "
                 "(there is no non-HIP fallback)")
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():

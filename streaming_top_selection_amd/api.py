@@ -80,6 +80,17 @@ def plan(B, S, T, H=64, D=128, m=4, k=512, q_pos0=0, kc_dtype="bf16", key_tile=0
                 out.n_chunks, out.cand_capacity, out.workspace_bytes)
 
 
+def workspace_bytes(B, S, T, H=64, D=128, m=4, k=512, key_tile=0, query_chunk=0,
+                    key_partition=0) -> int:
+    """si_indexer_topk_workspace_bytes: workspace bytes for q_pos0 = 0 (host only)."""
+    lib = _lib.load()
+    cfg = _cfg(key_tile, query_chunk, key_partition)
+    n = lib.si_indexer_topk_workspace_bytes(B, S, T, H, D, m, k, ctypes.byref(cfg))
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.SiError(_lib.SI_ERR_INVALID_ARG, lib.si_last_error().decode())
+    return int(n)
+
+
 def workspace(pl: Plan, device) -> torch.Tensor:
     """A workspace tensor (uint8) large enough for the plan."""
     return torch.empty(max(pl.workspace_bytes, 1), dtype=torch.uint8, device=device)

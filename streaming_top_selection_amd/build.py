@@ -1,6 +1,7 @@
 """Builds ``libsi_indexer.so`` (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m streaming_top_selection_amd.build
+    python streaming_top_selection_amd/build.py   (run by path: importing the package
+                                                  loads the library it builds)
 
 Every ``csrc/*.hip`` source is compiled with hipcc to an object in parallel, then the
 objects are linked into ``streaming_top_selection_amd/libsi_indexer.so``.

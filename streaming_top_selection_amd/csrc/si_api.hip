@@ -158,6 +158,15 @@ si_status si_indexer_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
     return SI_OK;
 }
 
+size_t si_indexer_topk_workspace_bytes(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
+                                       int32_t m, int32_t k, const si_config* cfg) {
+    g_last_error.clear();
+    si::PlanInternal pl;
+    // the key dtype does not change the plan; bf16 passes the dtype check
+    if (plan_or_fail(B, S, T, H, D, m, k, 0, SI_BF16, cfg, pl) != SI_OK) return SIZE_MAX;
+    return (size_t)pl.pub.workspace_bytes;
+}
+
 si_status si_indexer_select_chunk(const void* q, si_dtype q_dtype, const void* kc,
                                   si_dtype kc_dtype, const float* kc_scale, const float* w,
                                   int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,

@@ -102,15 +102,23 @@ def _channel_scales(spec, device):
 
 
 def gen_q_rows(spec: InputSpec, r0: int = 0, r1: Optional[int] = None, device="cpu"):
-    """q rows [r0, r1) of every batch entry: bfloat16 [B, r1 - r0, H, D]."""
+    """q rows [r0, r1) of every batch entry: bfloat16 [B, r1 - r0, H, D].
+
+    Drawn and rounded one generator block at a time, so the float32 temporaries stay
+    at one block (128 MiB at H = 64, D = 128) whatever the number of rows."""
     r1 = spec.S if r1 is None else r1
     out = torch.empty((spec.B, r1 - r0, spec.H, spec.D), dtype=torch.bfloat16, device=device)
     cq = _channel_scales(spec, device)[0] if spec.channel_scale else None
     for b in range(spec.B):
-        x = _randn_rows(spec, _TID_Q, b, r0, r1, (spec.H, spec.D), device)
-        if cq is not None:
-            x = x * cq
-        out[b] = x.to(torch.bfloat16)
+        lo = r0
+        while lo < r1:
+            hi = min(r1, (lo // BLOCK_ROWS + 1) * BLOCK_ROWS)
+            x = _randn_rows(spec, _TID_Q, b, lo, hi, (spec.H, spec.D), device)
+            if cq is not None:
+                x = x * cq
+            out[b, lo - r0:hi - r0] = x.to(torch.bfloat16)
+            del x
+            lo = hi
     return out
 
 

@@ -21,7 +21,7 @@ import oracle
 
 
 def check_rows(gidx, gscore, rows, q_bits, kc_bits, w, m, k, *, kc_dtype="bf16",
-               kc_scale=None, q_pos0=0, b=0, recall_gate=0.998):
+               kc_scale=None, q_pos0=0, b=0, recall_gate=0.998, verbose=True):
     """gidx/gscore: [R, k] numpy GPU outputs for the query rows `rows` of batch b."""
     rows = list(rows)
     exact = oracle.score_rows(q_bits, kc_bits, w, m, kc_dtype=kc_dtype, kc_scale=kc_scale,
@@ -32,6 +32,7 @@ def check_rows(gidx, gscore, rows, q_bits, kc_bits, w, m, k, *, kc_dtype="bf16",
     recalls = []
     worst_rel = 0.0
     floor_used = 0
+    mismatches = 0
     for i, t in enumerate(rows):
         n = oracle.visible_count(q_pos0 + t, m, T)
         need = min(k, n)
@@ -50,10 +51,13 @@ def check_rows(gidx, gscore, rows, q_bits, kc_bits, w, m, k, *, kc_dtype="bf16",
         O = set(oi[:need].tolist())
         G = set(gi[:need].tolist())
         recalls.append(len(G & O) / len(O))
+        mismatches += len(G ^ O) // 2
         skth = exact[i, oi[need - 1]]
         for s in G ^ O:
             gap = abs(exact[i, s] - skth)
             if gap > 1e-3 * abs(skth):
+                # the floor only decides where the relative rule is narrower than it
+                assert 1e-3 * abs(skth) < 2 * beta[i, s], f"row {t}: floor used needlessly"
                 assert gap <= 2 * beta[i, s], f"row {t}: mismatch key {s} gap {gap}"
                 floor_used += 1
         ex = exact[i, gi[:need]]
@@ -65,8 +69,12 @@ def check_rows(gidx, gscore, rows, q_bits, kc_bits, w, m, k, *, kc_dtype="bf16",
         worst_rel = max(worst_rel, float(rel.max()))
     mean_recall = float(np.mean(recalls)) if recalls else 1.0
     assert mean_recall >= recall_gate, f"mean recall {mean_recall}"
-    return {"mean_recall": mean_recall, "min_recall": float(min(recalls)) if recalls else 1.0,
-            "rows": len(rows), "floor_used": floor_used, "worst_rel_err": worst_rel}
+    stats = {"mean_recall": mean_recall, "min_recall": float(min(recalls)) if recalls else 1.0,
+             "rows": len(rows), "floor_used": floor_used, "worst_rel_err": worst_rel,
+             "mismatches": mismatches}
+    if verbose:
+        print("[parity]", stats, flush=True)
+    return stats
 
 
 def check_score_block(gscores, rows, q_bits, kc_bits, w, m, *, kc_dtype="bf16", kc_scale=None,

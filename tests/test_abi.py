@@ -159,3 +159,24 @@ def test_python_binding_checks_shapes_without_a_device():
         si.indexer_topk(q, kc, torch.zeros((1, 8, 3)), 2, 2)
     with pytest.raises(TypeError):
         si.indexer_topk(q, kc.float(), torch.zeros((1, 8, 2)), 2, 2)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(S=1024, T=256, k=64), dict(B=2, S=8192, T=2048), dict(S=262144, T=65536),
+    dict(S=1048576, T=262144), dict(key_tile=64), dict(key_tile=1024, k=2048),
+    dict(query_chunk=1000), dict(S=8192, T=8192, m=1, k=64), dict(key_tile=256, key_partition=4096),
+    dict(S=0), dict(B=0),
+])
+def test_workspace_bytes_matches_plan(lib, kw):
+    """si_indexer_topk_workspace_bytes is the plan's workspace at q_pos0 = 0."""
+    from streaming_top_selection_amd import api
+    args = dict(B=1, S=65536, T=16384, H=64, D=128, m=4, k=512)
+    args.update(kw)
+    assert api.workspace_bytes(**args) == api.plan(**args).workspace_bytes
+
+
+def test_workspace_bytes_rejects(lib):
+    from streaming_top_selection_amd import SiError, api
+    with pytest.raises(SiError, match="2048"):
+        api.workspace_bytes(1, 1024, 256, k=4096)
+    assert b"2048" in lib.si_last_error()

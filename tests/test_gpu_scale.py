@@ -45,18 +45,38 @@ def oracle_rows(x, rows, b=0):
 
 
 def check_sampled(gi, gs, x, spec, rows, kc_dtype="bf16"):
-    """Oracle check of sampled rows: the oracle sees each row at its absolute offset."""
+    """Oracle check of sampled rows: the oracle sees each row at its absolute offset.
+    Every row gets the full check_rows treatment (scores within beta, mismatches within
+    the k-th-score rule); the floor and mismatch counts are summed and printed."""
     qb, kb, w, sc = oracle_rows(x, rows)
-    stats = []
+    stats, floor_used, mism, worst = [], 0, 0, 0.0
     for i, r in enumerate(rows):
         n = oracle.visible_count(r, spec.m, spec.T)     # the oracle only reads keys < n
         st = check_rows(gi[r:r + 1], gs[r:r + 1], [0], qb[:, i:i + 1], kb[:, :n],
                         w[:, i:i + 1], spec.m, gi.shape[1], kc_dtype=kc_dtype,
-                        kc_scale=None if sc is None else sc[:, :n], q_pos0=r, recall_gate=0.0)
+                        kc_scale=None if sc is None else sc[:, :n], q_pos0=r, recall_gate=0.0,
+                        verbose=False)
         stats.append(st["mean_recall"])
+        floor_used += st["floor_used"]
+        mism += st["mismatches"]
+        worst = max(worst, st["worst_rel_err"])
     mean = float(np.mean(stats))
+    say(f"{len(rows)} oracle rows: recall mean {mean} min {float(np.min(stats))}, "
+        f"mismatches {mism}, floor used {floor_used}, worst rel score err {worst:.3g}")
     assert mean >= 0.998, f"mean recall {mean}"
     return mean, float(np.min(stats))
+
+
+def check_blocks_vs_materialize(si, q_rows, kc, w_rows, kc_scale, spec, k, out, blocks,
+                                what, row_block=None):
+    """Bit-exact streaming == materialise on row blocks [r0, r1): the materialise path is
+    called on the block's q rows at their absolute offset q_pos0 = r0.  q_rows(r0, r1)
+    and w_rows(r0, r1) return the inputs of those rows."""
+    for r0, r1 in blocks:
+        mat = si.materialize_topk(q_rows(r0, r1), kc, w_rows(r0, r1), spec.m, k,
+                                  kc_scale=kc_scale, q_pos0=r0, row_block=row_block)
+        torch.cuda.synchronize()
+        assert_same((out[0][:, r0:r1], out[1][:, r0:r1]), mat, f"{what} rows {r0}..{r1}")
 
 
 def test_v4flash_layer(gpu_lib):
@@ -66,15 +86,14 @@ def test_v4flash_layer(gpu_lib):
     gi, gs = gpu_lib.indexer_topk(x["q"], x["kc"], x["w"], spec.m, spec.k)
     torch.cuda.synchronize()
     gin, gsn = gi[0].cpu().numpy(), gs[0].cpu().numpy()
-    rows = synth.sample_rows(spec, 48)
+    rows = synth.sample_rows(spec, 512)
     mean, mn = check_sampled(gin, gsn, x, spec, rows)
     say("v4flash recall mean", mean, "min", mn)
     # bit-exact against the materialise path on the last and a middle row block
-    for r0, r1 in ((spec.S - 512, spec.S), (30000, 30512)):
-        sl = {"q": x["q"][:, r0:r1].contiguous(), "kc": x["kc"], "w": x["w"][:, r0:r1].contiguous()}
-        mat = gpu_lib.materialize_topk(sl["q"], sl["kc"], sl["w"], spec.m, spec.k, q_pos0=r0)
-        torch.cuda.synchronize()
-        assert_same((gi[:, r0:r1], gs[:, r0:r1]), mat, f"v4flash rows {r0}..{r1}")
+    check_blocks_vs_materialize(
+        gpu_lib, lambda a, b: x["q"][:, a:b].contiguous(), x["kc"],
+        lambda a, b: x["w"][:, a:b].contiguous(), None, spec, spec.k, (gi, gs),
+        ((spec.S - 512, spec.S), (30000, 30512)), "v4flash")
     # non-padded entries: sum over rows of min(k, n_t)
     t = np.arange(spec.S)
     want = int(np.minimum(spec.k, np.minimum(spec.T, (t + 1) // spec.m)).sum())
@@ -122,7 +141,15 @@ def test_long_context_sweeps(gpu_lib):
             assert (err <= np.maximum(1e-3 * np.abs(ex[sel]), bt[sel])).all(), (k, r)
         return float(np.mean(rec)), float(np.min(rec))
 
+    q_rows = lambda a, b: x["q"][:, a:b].contiguous()          # noqa: E731
+    w_rows = lambda a, b: x["w"][:, a:b].contiguous()          # noqa: E731
+    blocks = ((spec.S - 512, spec.S), (131072, 131584))
+
     base = cell(512, key_tile=512, query_chunk=4096)
+    # every key_tile / query_chunk cell equals base bit for bit (below), so this also
+    # checks each of them against the materialise path
+    check_blocks_vs_materialize(gpu_lib, q_rows, x["kc"], w_rows, None, spec, 512, base,
+                                blocks, "long base")
     report = {"base": recall(*base, 512)}
     for kt in (64, 128, 256, 1024):
         out = cell(512, key_tile=kt, query_chunk=4096)
@@ -135,6 +162,8 @@ def test_long_context_sweeps(gpu_lib):
     for k in (128, 256, 1024, 2048):
         out = cell(k, key_tile=512, query_chunk=4096)
         report[f"k={k}"] = recall(*out, k)
+        check_blocks_vs_materialize(gpu_lib, q_rows, x["kc"], w_rows, None, spec, k, out,
+                                    blocks, f"long k={k}")
         # a smaller k is a prefix of a larger one (same order, same ties)
         if k < 512:
             assert torch.equal(out[0], base[0][..., :k])
@@ -174,7 +203,13 @@ def test_million_token_capacity(gpu_lib):
     peak = torch.cuda.max_memory_allocated() - base_alloc
     say("million peak HBM bytes", peak)
     assert peak < 16e9
-    rows = synth.sample_rows(spec, 48)
+    # streaming == materialise bit for bit on an early and the last q slice (rows
+    # regenerated at their absolute offsets; 1024-row score blocks bound the buffer)
+    check_blocks_vs_materialize(
+        gpu_lib, lambda a, b: synth.gen_q_rows(spec, a, b, device=DEV), kc,
+        lambda a, b: w[:, a:b].contiguous(), kc_scale, spec, spec.k, (out_i, out_s),
+        ((20480, 24576), (spec.S - 4096, spec.S)), "million", row_block=1024)
+    rows = synth.sample_rows(spec, 128)
     # oracle inputs for the sampled rows: regenerate exactly those q rows
     qrows = torch.cat([synth.gen_q_rows(spec, r, r + 1, device=DEV) for r in rows], dim=1)
     qb = host_bits(qrows)
@@ -182,12 +217,15 @@ def test_million_token_capacity(gpu_lib):
     wb = w[:, rows].cpu().numpy()
     sc = kc_scale.cpu().numpy()
     gin, gsn = out_i[0].cpu().numpy(), out_s[0].cpu().numpy()
-    rec = []
+    rec, floor_used, mism = [], 0, 0
     for i, r in enumerate(rows):
         n = oracle.visible_count(r, spec.m, spec.T)
         st = check_rows(gin[r:r + 1], gsn[r:r + 1], [0], qb[:, i:i + 1], kb[:, :n],
                         wb[:, i:i + 1], spec.m, spec.k, kc_dtype="e4m3fn", kc_scale=sc[:, :n],
-                        q_pos0=r, recall_gate=0.0)
+                        q_pos0=r, recall_gate=0.0, verbose=False)
         rec.append(st["mean_recall"])
-    say("million recall mean", float(np.mean(rec)), "min", float(np.min(rec)))
+        floor_used += st["floor_used"]
+        mism += st["mismatches"]
+    say("million recall mean", float(np.mean(rec)), "min", float(np.min(rec)),
+        "rows", len(rows), "mismatches", mism, "floor used", floor_used)
     assert float(np.mean(rec)) >= 0.998

@@ -288,6 +288,106 @@ def test_fp32_evaluation_stays_inside_error_bound():
             assert abs(float(acc) - exact[i, s]) <= bound[i, s]
 
 
+def _worst_case_inputs(H, D=128, kc_dtype="bf16"):
+    """A score whose sequential fp32 evaluation loses half an ulp at every addition.
+
+    Head 0: q = (1, 2^-12, ..., 2^-12), key = (1, 2^-12, ..., 2^-12), w = 1, so its dot is
+    1 + (D-1) 2^-24 and each of the D-1 small products (2^-24, half an ulp of 1) rounds
+    away (round to nearest even).  Heads 1..H-1: q = 2^-12 e_0 and w = 2^-12, so each
+    adds 2^-24 to a running sum of 1 and rounds away again.  The exact score is
+    1 + (D + H - 2) 2^-24, the fp32 one is 1: the error is (D + H - 2) 2^-24.  With E4M3
+    keys the small key entries are the smallest subnormal 2^-9 (byte 0x01), q's small
+    entries 2^-15, and the key scale 1.0, so every product is the same."""
+    q = np.zeros((1, 1, H, D), dtype=np.float32)
+    w = np.zeros((1, 1, H), dtype=np.float32)
+    small_q = 2.0 ** -12 if kc_dtype == "bf16" else 2.0 ** -15
+    q[0, 0, 0, 0] = 1.0
+    q[0, 0, 0, 1:] = small_q
+    w[0, 0, 0] = 1.0
+    for h in range(1, H):
+        q[0, 0, h, 0] = 2.0 ** -12
+        w[0, 0, h] = 2.0 ** -12
+    qb = bits(torch.from_numpy(q).to(torch.bfloat16))
+    if kc_dtype == "bf16":
+        k = np.full((1, 1, D), 2.0 ** -12, dtype=np.float32)
+        k[0, 0, 0] = 1.0
+        kb, ks = bits(torch.from_numpy(k).to(torch.bfloat16)), None
+    else:
+        kb = np.full((1, 1, D), 0x01, dtype=np.uint8)       # 2^-9
+        kb[0, 0, 0] = 0x38                                   # 1.0 (exponent 7 = bias)
+        ks = np.ones((1, 1), dtype=np.float32)
+    return qb, kb, w, ks
+
+
+def _sequential_fp32(qb, kb, w, kc_dtype="bf16", ks=None):
+    """The score of query 0 and key 0 evaluated in fp32 the plain way: each dot product
+    summed left to right with fp32 rounding, then acc = fma(w_h, max(z_h, 0), acc)."""
+    qf = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).float().numpy()[0, 0]
+    if kc_dtype == "bf16":
+        kf = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).float().numpy()[0, 0]
+    else:
+        kf = torch.from_numpy(kb).view(torch.float8_e4m3fn).float().numpy()[0, 0]
+    H, D = qf.shape
+    acc = np.float32(0)
+    for h in range(H):
+        z = np.float32(0)
+        for d in range(D):
+            z = np.float32(z + np.float32(qf[h, d] * kf[d]))
+        if ks is not None:
+            z = np.float32(z * np.float32(ks[0, 0]))
+        # fma: the float64 product and sum of these values are exact; one rounding
+        acc = np.float32(np.float64(w[0, 0, h]) * np.float64(max(z, np.float32(0)))
+                         + np.float64(acc))
+    return float(acc)
+
+
+@pytest.mark.parametrize("kc_dtype", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("H", [1, 8, 64])
+def test_error_bound_is_tight_on_worst_case(H, kc_dtype):
+    """The fp32 forward-error bound is reached to within a few percent by a
+    constructed worst case, so it is neither loose nor too tight: a bound scaled by
+    2 or by 1/2 fails here."""
+    D = 128
+    qb, kb, w, ks = _worst_case_inputs(H, D, kc_dtype)
+    exact = oracle.score_rows(qb, kb, w, 1, kc_dtype=kc_dtype, kc_scale=ks)[0, 0]
+    beta = oracle.score_error_bound(qb, kb, w, 1, kc_dtype=kc_dtype, kc_scale=ks)[0, 0]
+    got = _sequential_fp32(qb, kb, w, kc_dtype, ks)
+    u = 2.0 ** -24
+    assert exact == 1.0 + (D + H - 2) * u                   # exact in float64
+    assert got == 1.0
+    err = exact - got
+    assert err <= beta
+    assert err >= 0.95 * beta, (err / beta)
+
+
+def test_error_bound_closed_form_all_ones():
+    """All-ones q, keys and weights: sum_h |w_h| sum_d |q k| = H D, so the bound is
+    (D + H + 2) 2^-24 H D."""
+    for H in (1, 3, 64):
+        D = 128
+        qb = bits(torch.ones((1, 1, H, D), dtype=torch.bfloat16))
+        kb = bits(torch.ones((1, 2, D), dtype=torch.bfloat16))
+        w = np.ones((1, 1, H), dtype=np.float32)
+        beta = oracle.score_error_bound(qb, kb, w, 1, q_pos0=1)[0]
+        assert (beta == (D + H + 2) * 2.0 ** -24 * H * D).all()
+
+
+@pytest.mark.parametrize("m,q_pos0,S,T", [(1, 0, 9, 9), (4, 0, 40, 10), (4, 5, 23, 12),
+                                          (3, 0, 20, 4), (2, 7, 15, 30)])
+def test_score_rows_mask_matches_brute_force(m, q_pos0, S, T):
+    """-inf exactly where (s + 1) m > t + 1 for the absolute position t = q_pos0 + row
+    (brute force over every (row, key) pair), finite everywhere else."""
+    spec = synth.InputSpec(B=1, S=S, T=T, H=2, D=128, m=m, k=4, seed=31)
+    x = synth.make_inputs(spec)
+    rows = oracle.score_rows(bits(x["q"]), bits(x["kc"]), x["w"].numpy(), m, q_pos0=q_pos0)
+    want = np.zeros((S, T), dtype=bool)
+    for r in range(S):
+        for s in range(T):
+            want[r, s] = (s + 1) * m > q_pos0 + r + 1
+    assert (np.isneginf(rows) == want).all()
+    assert np.isfinite(rows[~want]).all()
+
+
 # ---------------------------------------------------------------------------
 # Planted mistakes: every one must be caught by a pin above
 # ---------------------------------------------------------------------------
@@ -324,9 +424,43 @@ def _bad_bias_table():
     return t * 2.0
 
 
+def _bound_scaled(factor):
+    orig = OI.score_error_bound
+
+    def f(*a, **kw):
+        return orig(*a, **kw) * factor
+    return f
+
+
+def _run_pins(pins):
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    return caught
+
+
+def _hand_pins():
+    return [lambda c=c: _check_hand(c) for c in CASES]
+
+
+def _bound_pins():
+    return [lambda H=H, dt=dt: test_error_bound_is_tight_on_worst_case(H, dt)
+            for H in (1, 8, 64) for dt in ("bf16", "e4m3fn")]
+
+
+def _mask_pins():
+    return [lambda: test_score_rows_mask_matches_brute_force(4, 5, 23, 12),
+            lambda: test_score_rows_mask_matches_brute_force(3, 0, 20, 4)]
+
+
 @pytest.mark.parametrize("mutant", ["no_relu", "relu_after_weight", "no_scale",
-                                    "mask_off_by_one", "higher_index_first", "e4m3_bias"])
+                                    "mask_off_by_one", "higher_index_first", "e4m3_bias",
+                                    "bound_x2", "bound_half", "bound_no_head_term"])
 def test_planted_mistakes_are_caught(mutant, monkeypatch):
+    pins = _hand_pins()
     if mutant == "no_relu":
         monkeypatch.setattr(OI, "score_row", _no_relu)
     elif mutant == "relu_after_weight":
@@ -335,14 +469,27 @@ def test_planted_mistakes_are_caught(mutant, monkeypatch):
         monkeypatch.setattr(OI, "score_row", _no_scale)
     elif mutant == "mask_off_by_one":
         monkeypatch.setattr(OI, "visible_count", _mask_off_by_one)
+        # the mask of the written score rows is pinned on its own as well
+        assert _run_pins(_mask_pins()) > 0
     elif mutant == "higher_index_first":
         monkeypatch.setattr(OI, "select_topk", _higher_index_first)
     elif mutant == "e4m3_bias":
         monkeypatch.setattr(OI, "E4M3FN_TABLE", _bad_bias_table())
-    caught = 0
-    for case in CASES:
-        try:
-            _check_hand(case)
-        except AssertionError:
-            caught += 1
-    assert caught > 0, mutant
+    elif mutant == "bound_x2":
+        monkeypatch.setattr(OI, "score_error_bound", _bound_scaled(2.0))
+        monkeypatch.setattr(oracle, "score_error_bound", OI.score_error_bound)
+        pins = _bound_pins()
+    elif mutant == "bound_half":
+        monkeypatch.setattr(OI, "score_error_bound", _bound_scaled(0.5))
+        monkeypatch.setattr(oracle, "score_error_bound", OI.score_error_bound)
+        pins = _bound_pins()
+    elif mutant == "bound_no_head_term":
+        # a bound that forgets the head sum's additions: (D + 2) instead of (D + H + 2)
+        orig = OI.score_error_bound
+
+        def no_head(q_bits, kc_bits, w, m, **kw):
+            H = np.asarray(q_bits).shape[2]
+            return orig(q_bits, kc_bits, w, m, **kw) * (128 + 2) / (128 + H + 2)
+        monkeypatch.setattr(oracle, "score_error_bound", no_head)
+        pins = _bound_pins()
+    assert _run_pins(pins) > 0, mutant
