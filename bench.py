@@ -240,7 +240,7 @@ def main(argv=None):
         w0 = synth.gen_w_rows(spec, device=dev)
         torch.cuda.synchronize(dev)
         torch.cuda.reset_peak_memory_stats(dev)
-        cap_peak, cap_s, cap_n, cap_out = capacity_pass(si, spec, kc0, ks0, w0, dev)
+        cap_peak, cap_s, cap_n, capacity_outputs = capacity_pass(si, spec, kc0, ks0, w0, dev)
         capacity = {"peak_hbm_bytes": int(cap_peak), "peak_hbm_gb": cap_peak / 1e9,
                     "indexer_seconds": cap_s, "slices": cap_n, "slice_rows": CAPACITY_SLICE_ROWS,
                     "pairs_per_s": spec.B * visible_pairs(spec.S, spec.T, spec.m) / cap_s}
@@ -249,9 +249,6 @@ def main(argv=None):
         torch.cuda.empty_cache()
     x = synth.make_inputs(spec, device=dev)
     torch.cuda.synchronize(dev)
-    if capacity is not None:
-        # the streamed run's outputs must equal the resident-q run's (checked below)
-        capacity_outputs = cap_out
     # the peak of the timed work: inputs (already resident) + outputs + workspace; the
     # generator's temporaries are behind this reset
     torch.cuda.empty_cache()
