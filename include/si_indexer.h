@@ -29,7 +29,8 @@
  *    returns a message for the calling thread.  A launch failure returns SI_ERR_HIP.
  *  - Non-finite inputs (NaN, inf, E4M3 NaN bytes) are outside the contract.
  *  - Thread-safe: the library keeps no mutable global state besides the per-thread
- *    error message.
+ *    error message and the per-device address of si_indexer_topk_noalloc's scratch
+ *    (looked up once, under a lock).
  */
 #ifndef SI_INDEXER_H
 #define SI_INDEXER_H
@@ -139,6 +140,33 @@ si_status si_indexer_topk(const void* q, si_dtype q_dtype,
                           int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
                           int32_t* out_idx, float* out_score,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * si_indexer_topk_noalloc -- si_indexer_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and outputs, bit for bit, with the workspace taken
+ * from a static device array of SI_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * instead of a caller buffer.  No call here allocates or frees memory.
+ *
+ *  - The array exists once per device and is held until the process ends; its device
+ *    address is looked up on the first call on each device.
+ *  - The automatic query chunk (cfg NULL or query_chunk 0) is the largest whose
+ *    workspace fits the array.  A problem that does not fit even at 32 query rows per
+ *    chunk, or an explicit query_chunk that does not fit, returns SI_ERR_WORKSPACE
+ *    with the sizes in si_last_error().
+ *  - Every call on a device shares that device's array and leaves its contents behind:
+ *    calls that overlap on one device (different streams or threads, with no ordering
+ *    between them) race and give undefined results.  Calls ordered on one stream are
+ *    safe.  Nothing in the array needs to start at zero.
+ */
+#define SI_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype,
+                                  const void* kc, si_dtype kc_dtype, const float* kc_scale,
+                                  const float* w,
+                                  int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
+                                  int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
+                                  int32_t* out_idx, float* out_score, void* stream);
 
 /*
  * The two stages si_indexer_topk runs for query chunk `chunk` (0 <= chunk <

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsi_index
 
 SI_OK, SI_ERR_INVALID_ARG, SI_ERR_UNSUPPORTED, SI_ERR_WORKSPACE, SI_ERR_HIP = range(5)
 SI_BF16, SI_FP8_E4M3FN = 1, 2
+SI_NOALLOC_SCRATCH_BYTES = 256 << 20      # include/si_indexer.h
 
 
 class SiConfig(ctypes.Structure):
@@ -42,6 +43,8 @@ SIGNATURES = {
     "si_indexer_topk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _cfgp]),
     "si_indexer_topk": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,
                                _i32, _i64, _cfgp, _p, _p, _p, _sz, _p]),
+    "si_indexer_topk_noalloc": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32,
+                                       _i32, _i32, _i64, _cfgp, _p, _p, _p]),
     "si_indexer_select_chunk": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i64, _cfgp, _i32, _p, _sz, _p]),
     "si_indexer_merge_chunk": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _cfgp,

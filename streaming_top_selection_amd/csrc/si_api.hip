@@ -1,5 +1,6 @@
 // C ABI of the indexer library: validation, planning and the chunk driver.
 // All device work is enqueued on the caller's stream; nothing here allocates.
+#include <mutex>
 #include <string>
 
 #include "../../include/si_indexer.h"
@@ -8,9 +9,19 @@
 
 static_assert(si::kCandPad == si::kPlanCandPad, "candidate list padding");
 
+// Scratch of si_indexer_topk_noalloc (for callers that cannot allocate): one copy per
+// device, held for the life of the process.  Host code never uses the array's name as
+// an address (on the host it names a stand-in, not device memory): the device address
+// comes from hipGetSymbolAddress, once per device (scratch_on_current_device).
+static __device__ __align__(256) uint8_t scratch[SI_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 si_status fail(si_status st, const std::string& msg) {
     g_last_error = msg;
@@ -127,6 +138,25 @@ si_status run_merge(const si::PlanInternal& pl, int64_t B, int64_t S, int64_t T,
     return SI_OK;
 }
 
+// The device address of `scratch` on the current device, looked up on the first call
+// on each device and kept.
+si_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SI_ERR_UNSUPPORTED, "device index >= 64");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SI_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,6 +259,43 @@ si_status si_indexer_topk(const void* q, si_dtype q_dtype, const void* kc, si_dt
             return st;
         if ((st = run_merge(pl, B, S, T, m, k, q_pos0, c, out_idx, out_score, workspace, s)) !=
             SI_OK)
+            return st;
+    }
+    return SI_OK;
+}
+
+si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype, const void* kc,
+                                  si_dtype kc_dtype, const float* kc_scale, const float* w,
+                                  int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
+                                  int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
+                                  int32_t* out_idx, float* out_score, void* stream) {
+    g_last_error.clear();
+    si::PlanInternal pl;
+    std::string msg;
+    // the automatic query chunk is the largest whose workspace fits the scratch
+    si_status st = si::make_plan(B, S, T, H, D, m, k, q_pos0, kc_dtype, cfg, pl, msg,
+                                 (int64_t)SI_NOALLOC_SCRATCH_BYTES);
+    if (st != SI_OK) return fail(st, msg);
+    if ((st = check_inputs(q, q_dtype, kc, kc_dtype, kc_scale, w, B, S, T)) != SI_OK) return st;
+    if (B > 0 && S > 0 && (!out_idx || !out_score))
+        return fail(SI_ERR_INVALID_ARG, "outputs must not be NULL");
+    if (pl.pub.workspace_bytes > (int64_t)SI_NOALLOC_SCRATCH_BYTES)
+        return fail(SI_ERR_WORKSPACE,
+                    "the problem needs " + std::to_string(pl.pub.workspace_bytes) +
+                        " bytes of workspace per query chunk, more than the " +
+                        std::to_string((int64_t)SI_NOALLOC_SCRATCH_BYTES) +
+                        "-byte static scratch: use a smaller query_chunk, or si_indexer_topk "
+                        "with a caller workspace");
+    if (pl.pub.n_chunks == 0) return SI_OK;
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != SI_OK) return st;
+    // every count the merge reads is written by the select launch before it, so the
+    // scratch needs no clearing
+    const si::Problem P = make_problem(q, kc, kc_scale, w, B, S, T, H, m, q_pos0);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t c = 0; c < pl.pub.n_chunks; ++c) {
+        if ((st = run_select(pl, P, k, c, ws, kc_dtype == SI_FP8_E4M3FN, s)) != SI_OK) return st;
+        if ((st = run_merge(pl, B, S, T, m, k, q_pos0, c, out_idx, out_score, ws, s)) != SI_OK)
             return st;
     }
     return SI_OK;

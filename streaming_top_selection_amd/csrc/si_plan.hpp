@@ -55,9 +55,11 @@ inline si_status check_shape(int64_t B, int64_t S, int64_t T, int32_t H, int32_t
     return SI_OK;
 }
 
+// auto_cap: the workspace bound the automatic query chunk is chosen for
 inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D, int32_t m,
                            int32_t k, int64_t q_pos0, si_dtype kc_dtype, const si_config* cfg,
-                           PlanInternal& pl, std::string& msg) {
+                           PlanInternal& pl, std::string& msg,
+                           int64_t auto_cap = kAutoWorkspaceCap) {
     si_status st = check_shape(B, S, T, H, D, m, q_pos0, kc_dtype, msg);
     if (st != SI_OK) return st;
     if (k < 1) { msg = "k must be >= 1"; return SI_ERR_INVALID_ARG; }
@@ -118,7 +120,7 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
     if (c.query_chunk) {
         qc = round_up(c.query_chunk, kPlanTQ);
     } else {
-        qc = std::max<int64_t>(kPlanTQ, (kAutoWorkspaceCap / std::max<int64_t>(per_row, 1)) /
+        qc = std::max<int64_t>(kPlanTQ, (auto_cap / std::max<int64_t>(per_row, 1)) /
                                             kPlanTQ * kPlanTQ);
         qc = std::min<int64_t>(qc, std::max<int64_t>(round_up(S, kPlanTQ), kPlanTQ));
     }
