@@ -5,9 +5,12 @@ may import this package.  It shares no code with the HIP library.
 """
 
 from .indexer import (  # noqa: F401
+    E2M1_TABLE,
     E4M3FN_TABLE,
     bf16_bits_to_f64,
     e4m3fn_bits_to_f64,
+    e8m0_bits_to_f64,
+    mxfp4_bits_to_f64,
     indexer_topk,
     materialized_score_bytes,
     score_error_bound,
@@ -17,3 +20,4 @@ from .indexer import (  # noqa: F401
     total_visible_pairs,
     visible_count,
 )
+from .quant import E4M3_MAX, e4m3fn_encode_rne, quantize_q_e4m3  # noqa: F401,E402

@@ -79,6 +79,40 @@ def e4m3fn_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return E4M3FN_TABLE[np.asarray(bits).astype(np.uint8)]
 
 
+def _e2m1_value(c: int) -> float:
+    """Value of one OCP FP4 E2M1 code (OCP Microscaling Formats specification): 1 sign
+    bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent field 0 encodes the
+    subnormal m/2 * 2^(1-1); no infinities or NaN, so the largest value is 1.5 * 2^2."""
+    sign = -1.0 if (c & 0x8) else 1.0
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    if e == 0:
+        return sign * (m / 2.0)
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e8m0_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """OCP MX E8M0 scale bytes: 2^(b - 127); 0xFF is NaN."""
+    b = np.asarray(bits).astype(np.int64)
+    out = np.ldexp(1.0, b - 127)
+    return np.where(b == 255, np.nan, out)
+
+
+def mxfp4_bits_to_f64(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decode MXFP4 rows: packed [..., D/2] bytes (element 2i in the low nibble of byte
+    i, element 2i+1 in the high nibble) with one E8M0 scale per block of 32 elements,
+    scales [..., D/32].  Value = E2M1(code) * 2^(scale - 127) (OCP MX: each block of 32
+    elements shares one power-of-two scale)."""
+    p = np.asarray(packed).astype(np.uint8)
+    codes = np.stack([p & 0xF, p >> 4], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+    v = E2M1_TABLE[codes]
+    sc = np.repeat(e8m0_bits_to_f64(scales), 32, axis=-1)
+    return v * sc
+
+
 # ---------------------------------------------------------------------------
 # Mask and counts.
 # ---------------------------------------------------------------------------
@@ -111,7 +145,8 @@ def materialized_score_bytes(B: int, S: int, H: int, T: int) -> int:
 
 
 def _decode_keys(kc_bits, kc_dtype, kc_scale):
-    """Keys as float64 [B, T, D] and the per-row scale [B, T] (ones for bf16)."""
+    """Keys as float64 [B, T, D] and the per-row scale [B, T] (ones for bf16 and for
+    MXFP4, whose block scales are part of the decoded value)."""
     if kc_dtype == "bf16":
         kd = bf16_bits_to_f64(kc_bits)
         scale = np.ones(kd.shape[:2], dtype=np.float64)
@@ -120,9 +155,24 @@ def _decode_keys(kc_bits, kc_dtype, kc_scale):
         if kc_scale is None:
             raise ValueError("fp8 keys need a per-row scale")
         scale = np.asarray(kc_scale, dtype=np.float32).astype(np.float64)
+    elif kc_dtype == "mxfp4":
+        if kc_scale is None:
+            raise ValueError("MXFP4 keys need their E8M0 block scales")
+        kd = mxfp4_bits_to_f64(kc_bits, kc_scale)
+        scale = np.ones(kd.shape[:2], dtype=np.float64)
     else:
         raise ValueError(f"unknown key dtype {kc_dtype!r}")
     return kd, scale
+
+
+def _decode_q(q_bits, q_dtype):
+    """Query rows as float64: bf16 bit patterns, or E4M3 bytes (quantised q, whose
+    scale the caller has folded into the head weights)."""
+    if q_dtype == "bf16":
+        return bf16_bits_to_f64(q_bits)
+    if q_dtype == "e4m3fn":
+        return e4m3fn_bits_to_f64(q_bits)
+    raise ValueError(f"unknown q dtype {q_dtype!r}")
 
 
 def score_row(q_row: np.ndarray, w_row: np.ndarray, keys: np.ndarray,
@@ -152,13 +202,15 @@ def select_topk(scores: np.ndarray, k: int):
 
 
 def indexer_topk(q_bits, kc_bits, w, m: int, k: int, *, kc_dtype: str = "bf16",
-                 kc_scale=None, q_pos0: int = 0, rows=None):
+                 kc_scale=None, q_pos0: int = 0, rows=None, q_dtype: str = "bf16"):
     """Oracle top-k for the query rows ``rows`` (default: all) of every batch entry.
 
-    q_bits [B, S, H, D] bf16 bits, kc_bits [B, T, D] bf16 bits or E4M3 bytes,
-    w [B, S, H] float32, kc_scale [B, T] float32 for E4M3 keys.  Row r of q is the
-    absolute query position q_pos0 + r.  Returns idx int64 [B, R, k] and score float64
-    [B, R, k] for the R requested rows.
+    q_bits [B, S, H, D] bf16 bits (q_dtype "bf16") or E4M3 bytes ("e4m3fn", with w the
+    effective weights w * q_scale); kc_bits [B, T, D] bf16 bits or E4M3 bytes, or
+    [B, T, D/2] MXFP4 nibbles; w [B, S, H] float32; kc_scale [B, T] float32 for E4M3
+    keys, [B, T, D/32] E8M0 bytes for MXFP4 keys.  Row r of q is the absolute query
+    position q_pos0 + r.  Returns idx int64 [B, R, k] and score float64 [B, R, k] for
+    the R requested rows.
     """
     q_bits = np.asarray(q_bits)
     w = np.asarray(w, dtype=np.float32)
@@ -173,14 +225,14 @@ def indexer_topk(q_bits, kc_bits, w, m: int, k: int, *, kc_dtype: str = "bf16",
             n = visible_count(q_pos0 + int(r), m, T)
             if n == 0:
                 continue
-            qd = bf16_bits_to_f64(q_bits[b, r])
+            qd = _decode_q(q_bits[b, r], q_dtype)
             sc = score_row(qd, w[b, r].astype(np.float64), kd[b, :n], scale[b, :n])
             out_idx[b, i], out_val[b, i] = select_topk(sc, k)
     return out_idx, out_val
 
 
 def score_rows(q_bits, kc_bits, w, m: int, *, kc_dtype: str = "bf16", kc_scale=None,
-               q_pos0: int = 0, rows=None, b: int = 0):
+               q_pos0: int = 0, rows=None, b: int = 0, q_dtype: str = "bf16"):
     """Full score rows [R, T] of batch entry ``b`` in float64, -inf where masked.
 
     This is one [R, T] slice of the head-summed score tensor that the materialise
@@ -197,13 +249,14 @@ def score_rows(q_bits, kc_bits, w, m: int, *, kc_dtype: str = "bf16", kc_scale=N
         n = visible_count(q_pos0 + int(r), m, T)
         if n == 0:
             continue
-        qd = bf16_bits_to_f64(q_bits[b, r])
+        qd = _decode_q(q_bits[b, r], q_dtype)
         out[i, :n] = score_row(qd, w[b, r].astype(np.float64), kd[b, :n], scale[b, :n])
     return out
 
 
 def score_error_bound(q_bits, kc_bits, w, m: int, *, kc_dtype: str = "bf16",
-                      kc_scale=None, q_pos0: int = 0, rows=None, b: int = 0):
+                      kc_scale=None, q_pos0: int = 0, rows=None, b: int = 0,
+                      q_dtype: str = "bf16"):
     """Forward-error bound of an FP32 evaluation of each score, [R, T] float64.
 
     Textbook bound for a recursive sum of n terms in precision u = 2^-24:
@@ -211,6 +264,8 @@ def score_error_bound(q_bits, kc_bits, w, m: int, *, kc_dtype: str = "bf16",
     head (bf16 products are exact in fp32), scaled by the key scale, clamped at zero,
     then an H-term weighted sum, so the combined bound is
     (D + H + 2) * 2^-24 * sum_h |w_h| * scale_s * sum_d |q_hd k_sd|.
+    The same bound holds for E4M3 q (products of two E4M3 values, or of an E4M3 and an
+    MXFP4 value with its power-of-two block scale, are exact in fp32 as well).
     """
     q_bits = np.asarray(q_bits)
     w = np.asarray(w, dtype=np.float32)
@@ -224,7 +279,7 @@ def score_error_bound(q_bits, kc_bits, w, m: int, *, kc_dtype: str = "bf16",
         n = visible_count(q_pos0 + int(r), m, T)
         if n == 0:
             continue
-        qd = np.abs(bf16_bits_to_f64(q_bits[b, r]))
+        qd = np.abs(_decode_q(q_bits[b, r], q_dtype))
         za = (qd @ np.abs(kd[b, :n]).T) * scale[b, :n][None, :]
         out[i, :n] = (D + H + 2) * u * (np.abs(w[b, r].astype(np.float64)) @ za)
     return out

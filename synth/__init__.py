@@ -9,5 +9,6 @@ from .gen import (  # noqa: F401
     gen_q_rows,
     gen_w_rows,
     make_inputs,
+    mxfp4_quantize,
     sample_rows,
 )

@@ -37,7 +37,7 @@ class InputSpec:
     m: int = 4
     k: int = 512
     seed: int = 0
-    kc_dtype: str = "bf16"          # "bf16" or "e4m3fn" (+ per-row fp32 scale)
+    kc_dtype: str = "bf16"          # "bf16", "e4m3fn" (+ per-row fp32 scale) or "mxfp4"
     w_std: float = 1.0 / 8.0        # w ~ N(0, 1) * w_std
     channel_scale: Optional[tuple] = None   # (lo, hi): per-channel U(lo, hi) scales
     dup_frac: float = 0.0           # fraction of keys that copy an earlier key
@@ -57,7 +57,40 @@ CONFIGS = {
     "long": InputSpec(B=1, S=262144, T=65536, k=512, seed=4),
     # Million-token capacity run with E4M3 keys and a per-row fp32 scale.
     "million": InputSpec(B=1, S=1048576, T=262144, k=512, seed=5, kc_dtype="e4m3fn"),
+    # The V4-Flash layer with low-precision keys (the fp8-q paths quantise q themselves).
+    "v4flash-e4m3": InputSpec(B=1, S=65536, T=16384, k=512, seed=3, channel_scale=(0.5, 2.0),
+                              kc_dtype="e4m3fn"),
+    "v4flash-mxfp4": InputSpec(B=1, S=65536, T=16384, k=512, seed=3, channel_scale=(0.5, 2.0),
+                               kc_dtype="mxfp4"),
 }
+
+# E2M1 rounding boundaries: midpoints between the magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def mxfp4_quantize(x: torch.Tensor):
+    """OCP MX FP4 of float32 rows x [..., D] (D a multiple of 32), the recipe of the OCP
+    Microscaling Formats specification: each block of 32 elements gets the shared scale
+    2^(floor(log2(max |x|)) - 2) (2 = the largest E2M1 exponent), stored as the E8M0
+    byte exponent + 127; each element is x / scale rounded to the nearest E2M1 value
+    (ties to the even code), saturated at +-6.  Returns (packed uint8 [..., D/2],
+    element 2i in the low nibble of byte i; scales uint8 [..., D/32])."""
+    *lead, D = x.shape
+    xb = x.reshape(*lead, D // 32, 32).to(torch.float32)
+    amax = xb.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)                      # amax = f * 2^e, f in [0.5, 1)
+    shared = torch.where(amax > 0, e - 1 - 2, torch.full_like(e, -127)).clamp(-127, 127)
+    y = xb * torch.pow(2.0, -shared.to(torch.float32))[..., None]     # exact power of 2
+    a = y.abs().clamp(max=6.0)
+    code = torch.zeros_like(a, dtype=torch.int32)
+    for j, b in enumerate(_E2M1_MIDPOINTS):
+        code += (a > b).to(torch.int32)
+        if j % 2 == 1:                            # tie between codes j and j+1: take even j+1
+            code += (a == b).to(torch.int32)
+    code |= (torch.signbit(y).to(torch.int32) << 3)
+    code = code.reshape(*lead, D).to(torch.uint8)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), (shared + 127).to(torch.uint8).contiguous()
 
 
 def _mix(*parts: int) -> int:
@@ -157,6 +190,8 @@ def gen_keys(spec: InputSpec, device="cpu"):
     """Compressed keys for every batch entry.
 
     bf16 keys: (kc bfloat16 [B, T, D], None).
+    mxfp4 keys: (kc uint8 [B, T, D/2] packed E2M1 codes, kc_scale uint8 [B, T, D/32]
+    E8M0 block scales), see mxfp4_quantize.
     e4m3fn keys: (kc uint8 [B, T, D] holding OCP E4M3 bytes, kc_scale float32 [B, T]),
     where scale = max_d |x| / 448 and the byte is E4M3(round-to-nearest-even of
     clamp(x / scale, -448, 448)).  The clamp matters: torch's cast does not saturate.
@@ -178,6 +213,8 @@ def gen_keys(spec: InputSpec, device="cpu"):
         scale = torch.where(scale > 0, scale, torch.ones_like(scale))
         y = torch.clamp(x / scale[..., None], -448.0, 448.0)
         return y.to(torch.float8_e4m3fn).view(torch.uint8), scale.to(torch.float32)
+    if spec.kc_dtype == "mxfp4":
+        return mxfp4_quantize(x)
     raise ValueError(f"unknown key dtype {spec.kc_dtype!r}")
 
 
