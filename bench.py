@@ -30,6 +30,7 @@ import time
 
 METRIC = "indexer scored q·k pairs/s + peak HBM at S=64K V4-Flash; % MFMA peak"
 BF16_DENSE_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP8_DENSE_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (the f8f6f4 ops on E4M3)
 HBM_PEAK_GBPS = 8000.0              # MI355X HBM3E
 
 WORKLOADS = {
@@ -41,7 +42,19 @@ WORKLOADS = {
     "long": "Long-context: B=1, S=262144, m=4, T=65536, H_I=64, D=128, top-k=512, bf16 q/k",
     "million": "Million-token capacity: B=1, S=1048576, m=4, T=262144, H_I=64, D=128, top-k=512, "
                "bf16 q, E4M3 keys with per-row fp32 scale",
+    "v4flash-fp8": "V4-Flash indexer layer with fp8 operands: B=1, S=65536, m=4, T=16384, H_I=64, "
+                   "D=128, top-k=512; q quantised per (row, head) to E4M3 inside the step (scale "
+                   "folded into w), keys E4M3 with per-row fp32 scale (per-channel U(0.5,2) data), "
+                   "f8f6f4 MFMA",
+    "v4flash-mxfp4": "V4-Flash indexer layer with MXFP4 keys: B=1, S=65536, m=4, T=16384, H_I=64, "
+                     "D=128, top-k=512; q quantised per (row, head) to E4M3 inside the step, keys "
+                     "MXFP4 (E2M1 + E8M0 per 32), scaled f8f6f4 MFMA",
 }
+# workload -> input configuration (synth.CONFIGS); the fp8-q workloads quantise q in the step
+WORKLOAD_SPEC = {"v4flash-fp8": "v4flash-e4m3", "v4flash-mxfp4": "v4flash-mxfp4"}
+FP8_Q = {"v4flash-fp8", "v4flash-mxfp4"}
+DTYPE_NAME = {("bf16", "bf16"): "bf16", ("bf16", "e4m3fn"): "bf16",
+              ("e4m3fn", "e4m3fn"): "e4m3", ("e4m3fn", "mxfp4"): "e4m3xe2m1"}
 # default (steps, warmup) per workload: about a minute of timed work at most
 DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1)}
 # q rows per slice of the million workload's streamed-q capacity pass
@@ -49,8 +62,8 @@ CAPACITY_SLICE_ROWS = 16384
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["si_select.hpp", "si_select_kt512_bf16.hip", "si_compact.hpp", "si_score.hpp",
-                  "si_common.hpp"]
+KERNEL_SOURCES = ["si_select.hpp", "si_select_inst.hip", "si_compact.hpp", "si_score.hpp",
+                  "si_score_q8.hpp", "si_common.hpp"]
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_v4flash_s65536.md")
 COPY_PROBE_BYTES = 1 << 30
 
@@ -143,8 +156,9 @@ def capacity_pass(si, spec, kc, kc_scale, w, dev, slice_rows=CAPACITY_SLICE_ROWS
     return torch.cuda.max_memory_allocated(dev), busy, n, out
 
 
-def cpu_baseline(spec, x, seconds, seed=100):
-    """Time the float64 oracle on sampled query rows (roughly `seconds` of work)."""
+def cpu_baseline(spec, x, seconds, seed=100, fp8_q=False):
+    """Time the float64 oracle on sampled query rows (roughly `seconds` of work).  With
+    fp8_q the oracle quantises each row's q itself, then scores the E4M3 operands."""
     import numpy as np
     import torch
 
@@ -165,7 +179,7 @@ def cpu_baseline(spec, x, seconds, seed=100):
     kc_bits = (kc_cpu.numpy() if kc_cpu.dtype == torch.uint8
                else kc_cpu.view(torch.int16).numpy().view(np.uint16))
     kc_scale = None if x["kc_scale"] is None else x["kc_scale"].cpu().numpy()
-    kc_dtype = "bf16" if x["kc_scale"] is None else "e4m3fn"
+    kc_dtype = spec.kc_dtype
     done_pairs, done_rows, checked = 0, [], []
     t0 = time.perf_counter()
     while rows and time.perf_counter() - t0 < seconds:
@@ -173,8 +187,12 @@ def cpu_baseline(spec, x, seconds, seed=100):
         qb = x["q"][:, r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
         wb = x["w"][:, r:r + 1].cpu().numpy()
         t1 = time.perf_counter()
+        q_dtype = "bf16"
+        if fp8_q:
+            qb, wb, _ = oracle.quantize_q_e4m3(qb, wb)
+            q_dtype = "e4m3fn"
         idx, _ = oracle.indexer_topk(qb, kc_bits, wb, spec.m, spec.k, kc_dtype=kc_dtype,
-                                     kc_scale=kc_scale, q_pos0=r)
+                                     kc_scale=kc_scale, q_pos0=r, q_dtype=q_dtype)
         checked.append((r, idx[0, 0]))
         done_pairs += spec.B * oracle.visible_count(r, spec.m, spec.T)
         done_rows.append(time.perf_counter() - t1)
@@ -186,8 +204,8 @@ def cpu_baseline(spec, x, seconds, seed=100):
         "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{len(done_rows)} query rows sampled uniformly over rows that see >= k keys "
-                  f"(seed {seed}), float64 NumPy oracle, {done_pairs} visible pairs in "
-                  f"{elapsed:.1f} s",
+                  f"(seed {seed}), float64 NumPy oracle{' (q quantised per row)' if fp8_q else ''}, "
+                  f"{done_pairs} visible pairs in {elapsed:.1f} s",
     }, checked
 
 
@@ -231,7 +249,8 @@ def main(argv=None):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    spec = synth.CONFIGS[args.workload]
+    spec = synth.CONFIGS[WORKLOAD_SPEC.get(args.workload, args.workload)]
+    fp8_q = args.workload in FP8_Q
     capacity = None
     if args.workload == "million" and args.mode == "bench":
         # q streamed in slices, never resident whole: the peak HBM of the pages' capacity
@@ -255,7 +274,7 @@ def main(argv=None):
     torch.cuda.reset_peak_memory_stats(dev)
     free0, total_mem = torch.cuda.mem_get_info(dev)
     input_bytes = tensor_bytes(x["q"], x["kc"], x["kc_scale"], x["w"])
-    kc_dtype = "bf16" if x["kc_scale"] is None else "e4m3fn"
+    kc_dtype = spec.kc_dtype
     knobs = dict(key_tile=args.key_tile, query_chunk=args.query_chunk,
                  key_partition=args.key_partition)
     pl = si.plan(spec.B, spec.S, spec.T, spec.H, spec.D, spec.m, spec.k, 0, kc_dtype, **knobs)
@@ -264,12 +283,29 @@ def main(argv=None):
            torch.empty((spec.B, spec.S, spec.k), dtype=torch.float32, device=dev))
     output_bytes = tensor_bytes(*out)
     stream = torch.cuda.current_stream(dev)
+    # the scorer's operands: bf16 q and w, or (fp8 q) the quantiser's outputs, rewritten
+    # by the quantise kernel at the start of every step
+    if fp8_q:
+        qop = (torch.empty(x["q"].shape, dtype=torch.uint8, device=dev),
+               torch.empty(x["w"].shape, dtype=torch.float32, device=dev))
+        output_bytes += tensor_bytes(*qop)
+    else:
+        qop = (x["q"], x["w"])
+    quant_events = []
 
     def step(events=None):
+        if fp8_q:
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            si.quantize_q(x["q"], x["w"], out=qop)
+            if events is not None:
+                e1.record(stream)
+                quant_events.append((e0, e1))
         for c in range(pl.n_chunks):
             if events is not None:
                 events[c][0].record(stream)
-            si.indexer_select_chunk(x["q"], x["kc"], x["w"], spec.m, spec.k, c, ws,
+            si.indexer_select_chunk(qop[0], x["kc"], qop[1], spec.m, spec.k, c, ws,
                                     kc_scale=x["kc_scale"], **knobs)
             if events is not None:
                 events[c][1].record(stream)
@@ -281,7 +317,7 @@ def main(argv=None):
     if args.mode == "select-once":
         step()
         torch.cuda.synchronize(dev)
-        si.indexer_select_chunk(x["q"], x["kc"], x["w"], spec.m, spec.k, 0, ws,
+        si.indexer_select_chunk(qop[0], x["kc"], qop[1], spec.m, spec.k, 0, ws,
                                 kc_scale=x["kc_scale"], **knobs)
         torch.cuda.synchronize(dev)
         print("select-once done", flush=True)
@@ -297,7 +333,7 @@ def main(argv=None):
 
     # the staged step is the product call: check once against si_indexer_topk itself
     step()
-    ref = si.indexer_topk(x["q"], x["kc"], x["w"], spec.m, spec.k, kc_scale=x["kc_scale"],
+    ref = si.indexer_topk(qop[0], x["kc"], qop[1], spec.m, spec.k, kc_scale=x["kc_scale"],
                           out=(torch.empty_like(out[0]), torch.empty_like(out[1])), ws=ws,
                           **knobs)
     torch.cuda.synchronize(dev)
@@ -347,6 +383,8 @@ def main(argv=None):
     kept = int(np.minimum(spec.k, np.minimum(spec.T, (t + 1) // spec.m)).sum()) * spec.B
     merge_bytes = kept * 8 + spec.B * spec.S * pl.n_partitions * 4 + spec.B * spec.S * spec.k * 8
     merge_gbps = merge_bytes / mrg_step_s / 1e9
+    peak_tflops = FP8_DENSE_PEAK_TFLOPS if fp8_q else BF16_DENSE_PEAK_TFLOPS
+    q_dtype = "e4m3fn" if fp8_q else "bf16"
 
     traffic = committed_traffic() if args.workload == "v4flash" and not any(knobs.values()) \
         else None
@@ -361,29 +399,31 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_NAME[(q_dtype, kc_dtype)],
         "data": "synthetic",
         "config": {
             "workload": WORKLOADS[args.workload],
             "B": spec.B, "S": spec.S, "T": spec.T, "H_I": spec.H, "D": spec.D, "m": spec.m,
-            "k": spec.k, "key_dtype": kc_dtype, "key_tile": pl.key_tile,
+            "k": spec.k, "q_dtype": q_dtype, "key_dtype": kc_dtype, "key_tile": pl.key_tile,
             "query_chunk": pl.query_chunk, "key_partition": pl.key_partition,
             "n_partitions": pl.n_partitions, "n_chunks": pl.n_chunks,
         },
         "visible_pairs": pairs,
-        "mfma_frac": achieved_tflops / BF16_DENSE_PEAK_TFLOPS,
+        "mfma_frac": achieved_tflops / peak_tflops,
         "peak_hbm_bytes": int(peak_alloc),
         "peak_hbm_gib": peak_alloc / 2 ** 30,
         "hbm_bytes": {"inputs": input_bytes, "outputs": output_bytes,
                       "workspace": int(ws.numel()), "allocator_peak_timed": int(peak_alloc)},
         "device_mem_delta_bytes": int(free0 - free1),
         "roofline": {
-            "kernel": "select_kernel (fused bf16 MFMA scoring + running top-k)",
+            "kernel": ("select_kernel (fused E4M3 f8f6f4-MFMA scoring + running top-k)"
+                       if fp8_q else "select_kernel (fused bf16 MFMA scoring + running top-k)"),
             "bound": "mfma",
             "achieved": achieved_tflops,
-            "peak": BF16_DENSE_PEAK_TFLOPS,
+            "peak": peak_tflops,
+            "peak_dtype": "fp8 dense" if fp8_q else "bf16 dense",
             "unit": "TFLOP/s",
-            "frac": achieved_tflops / BF16_DENSE_PEAK_TFLOPS,
+            "frac": achieved_tflops / peak_tflops,
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "mean_launch_ms": sel_mean_s * 1e3,
             "launches_per_step": pl.n_chunks,
@@ -398,10 +438,21 @@ def main(argv=None):
             "mean_launch_ms": mrg_mean_s * 1e3, "bytes_per_step": merge_bytes,
         },
     }
+    if fp8_q:
+        # quantise: read bf16 q + w, write E4M3 q + w_eff (HBM-bound)
+        nvec = spec.B * spec.S * spec.H
+        qbytes = nvec * spec.D * 3 + nvec * 8
+        qt = [a.elapsed_time(b) for a, b in quant_events] or [float("nan")]
+        qmean = sum(qt) / len(qt) / 1e3
+        rec["quantize"] = {"kernel": "quantize_q_kernel (per-(row, head) E4M3 q, w * scale)",
+                           "bound": "hbm", "achieved": qbytes / qmean / 1e9,
+                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": qbytes / qmean / 1e9 / HBM_PEAK_GBPS,
+                           "mean_launch_ms": qmean * 1e3, "bytes_per_step": qbytes}
     if capacity is not None:
         rec["streamed_q_capacity_run"] = capacity
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
-        base, checked = cpu_baseline(spec, x, args.cpu_seconds)
+        base, checked = cpu_baseline(spec, x, args.cpu_seconds, fp8_q=fp8_q)
         rec["cpu_baseline"] = base
         got = out[0][0].cpu().numpy()
         hits = [len((set(got[r].tolist()) & set(o.tolist())) - {-1}) /
@@ -409,6 +460,21 @@ def main(argv=None):
         rec["oracle_sample_recall"] = {"rows": len(checked),
                                        "mean": float(np.mean(hits)) if hits else None,
                                        "min": float(np.min(hits)) if hits else None}
+        if fp8_q:
+            # the quantisation's own effect: the same rows against the oracle of the
+            # unquantised bf16 q (same keys)
+            import oracle
+            kc_c = x["kc"].cpu().numpy()
+            ks_c = x["kc_scale"].cpu().numpy()
+            rb = []
+            for r, _ in checked[:64]:
+                qb = x["q"][:, r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+                oi, _ = oracle.indexer_topk(qb, kc_c, x["w"][:, r:r + 1].cpu().numpy(), spec.m,
+                                            spec.k, kc_dtype=kc_dtype, kc_scale=ks_c, q_pos0=r)
+                o = set(oi[0, 0].tolist()) - {-1}
+                rb.append(len(set(got[r].tolist()) & o) / max(1, len(o)))
+            rec["recall_vs_bf16_q_oracle"] = {"rows": len(rb), "mean": float(np.mean(rb)),
+                                              "min": float(np.min(rb))}
     print(json.dumps(rec), flush=True)
     return 0
 

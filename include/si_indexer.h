@@ -11,10 +11,17 @@
  *
  * Score (the pages print no formula; the DeepSeek lightning-indexer form is used):
  *     I[b,t,s] = sum_h w[b,t,h] * max(0, scale[b,s] * sum_d q[b,t,h,d] * kc[b,s,d])
- * with scale = 1 for bf16 keys.  Rounding order on the GPU, identical in every entry
- * point and for every tuning knob: bf16 x bf16 products accumulated in fp32 by one
- * fixed MFMA sequence per head, then acc = fmaf(w_h, max(z_h, 0), acc) for h = 0..H-1
- * starting from +0, then (E4M3 keys) acc * scale[s]; a -0 result is reported as +0.
+ * with scale = 1 for bf16 keys, the per-row fp32 scale for E4M3 keys, and for MXFP4
+ * keys kc[b,s,d] = E2M1 * 2^(E8M0 of d's block - 127) with scale = 1.  Operands:
+ *   q bf16 x keys bf16 or E4M3 (E4M3 widened exactly to bf16): bf16 MFMA;
+ *   q E4M3 x keys E4M3 or MXFP4: the f8f6f4 MFMA (lower indexer precision: jeff.news
+ *   page, 기술 맥락; MXFP4 indexer keys: chengshu page, 部署视角).  E4M3 q is q
+ *   quantised per (row, head) with its scale folded into w (si_quantize_q_e4m3), so
+ *   w is then the effective weight w * q_scale.
+ * Rounding order on the GPU, identical in every entry point and for every tuning knob
+ * of one operand pair: the products (exact in fp32) accumulated by one fixed MFMA
+ * sequence per head, then acc = fmaf(w_h, max(z_h, 0), acc) for h = 0..H-1 starting
+ * from +0, then (E4M3 keys) acc * scale[s]; a -0 result is reported as +0.
  * Causal mask: key s is visible to query row r iff (s + 1) * m <= q_pos0 + r + 1.
  * Order: by (score descending, key index ascending), so the top-k is unique.
  *
@@ -42,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SI_ABI_VERSION 1
+#define SI_ABI_VERSION 2
 
 typedef enum si_status {
     SI_OK = 0,
@@ -54,7 +61,10 @@ typedef enum si_status {
 
 typedef enum si_dtype {
     SI_BF16 = 1,              /* bfloat16                                          */
-    SI_FP8_E4M3FN = 2         /* OCP FP8 E4M3 (bias 7, no inf, max 448): keys only */
+    SI_FP8_E4M3FN = 2,        /* OCP FP8 E4M3 (bias 7, no inf, max 448): q or keys */
+    SI_MXFP4_E2M1 = 3         /* OCP MXFP4: E2M1 elements, two per byte (element 2i
+                                 in the low nibble of byte i), one E8M0 scale byte
+                                 per 32 elements: keys only, with E4M3 q           */
 } si_dtype;
 
 /* Tuning knobs; 0 selects the automatic value.  No knob changes any output bit
@@ -116,10 +126,13 @@ size_t si_indexer_topk_workspace_bytes(int64_t B, int64_t S, int64_t T, int32_t 
 /*
  * si_indexer_topk -- streaming top-k of the indexer scores (the hot path).
  *
- *  q         [B, S, H, D] bf16 query rows; row r is absolute position q_pos0 + r
- *  kc        [B, T, D]    compressed keys, bf16 or E4M3 bytes (kc_dtype)
- *  kc_scale  [B, T] fp32  per-key scale for E4M3 keys (> 0); must be NULL for bf16
- *  w         [B, S, H]    fp32 head weights
+ *  q         [B, S, H, D] query rows, bf16 or E4M3 bytes (q_dtype); row r is absolute
+ *            position q_pos0 + r
+ *  kc        [B, T, D]    compressed keys, bf16 or E4M3 bytes (kc_dtype), or
+ *            [B, T, D/2]  MXFP4 packed E2M1 codes
+ *  kc_scale  E4M3 keys: [B, T] fp32 per-key scale (> 0); MXFP4 keys: [B, T, D/32]
+ *            E8M0 bytes (4-byte aligned); must be NULL for bf16 keys
+ *  w         [B, S, H]    fp32 head weights (E4M3 q: the effective w * q_scale)
  *  m         compression ratio (>= 1), used only by the causal mask
  *  k         keys kept per query, 1..2048
  *  q_pos0    absolute position of q row 0 (>= 0): lets a caller stream q in slices
@@ -129,12 +142,13 @@ size_t si_indexer_topk_workspace_bytes(int64_t B, int64_t S, int64_t T, int32_t 
  *  workspace device scratch of at least plan.workspace_bytes bytes (see
  *            si_indexer_plan), 256-byte aligned; its contents are clobbered
  *
- * Supported: D = 128, 1 <= H <= 128, 1 <= k <= 2048, q bf16, keys bf16 or E4M3,
- * 0 <= T < 2^31 - 1.  S = 0 or B = 0 is a no-op.
+ * Supported: D = 128, 1 <= H <= 128, 1 <= k <= 2048, 0 <= T < 2^31 - 1, and the
+ * operand pairs (q, keys): (bf16, bf16), (bf16, E4M3), (E4M3, E4M3), (E4M3, MXFP4).
+ * S = 0 or B = 0 is a no-op.
  * Enqueues, per query chunk, the fused score + select kernel and the merge kernel.
  */
 si_status si_indexer_topk(const void* q, si_dtype q_dtype,
-                          const void* kc, si_dtype kc_dtype, const float* kc_scale,
+                          const void* kc, si_dtype kc_dtype, const void* kc_scale,
                           const float* w,
                           int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                           int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
@@ -162,7 +176,7 @@ si_status si_indexer_topk(const void* q, si_dtype q_dtype,
 #define SI_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
 
 si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype,
-                                  const void* kc, si_dtype kc_dtype, const float* kc_scale,
+                                  const void* kc, si_dtype kc_dtype, const void* kc_scale,
                                   const float* w,
                                   int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                                   int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
@@ -183,7 +197,7 @@ si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype,
  *   out_idx / out_score (the merge-topk step of the same diagram).
  */
 si_status si_indexer_select_chunk(const void* q, si_dtype q_dtype,
-                                  const void* kc, si_dtype kc_dtype, const float* kc_scale,
+                                  const void* kc, si_dtype kc_dtype, const void* kc_scale,
                                   const float* w,
                                   int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                                   int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
@@ -198,6 +212,27 @@ si_status si_indexer_merge_chunk(int64_t B, int64_t S, int64_t T, int32_t H, int
                                  void* stream);
 
 /*
+ * si_quantize_q_e4m3 -- the operand preparation of the fp8 path: quantises each
+ * (row, head) vector of bf16 q to OCP E4M3 with its own fp32 scale and folds the scale
+ * into the head weight (lower indexer precision: jeff.news page, 기술 맥락):
+ *     scale    = max_d |q[r,h,d]| / 448  (1 for an all-zero vector)
+ *     q8[r,h,:] = E4M3(clamp(q[r,h,:] / scale, -448, 448)), round to nearest even
+ *     w_eff[r,h] = w[r,h] * scale
+ * each step one correctly rounded fp32 operation.  q8 and w_eff are then the q (q_dtype
+ * SI_FP8_E4M3FN) and w of si_indexer_topk: since the scale is positive,
+ * w * ReLU(scale * z) = w_eff * ReLU(z).
+ *
+ *  q       [rows, H, D] bf16 (rows = B * S), 8-byte aligned
+ *  w       [rows, H]    fp32
+ *  q8      [rows, H, D] E4M3 bytes out, 4-byte aligned
+ *  w_eff   [rows, H]    fp32 out
+ *  q_scale [rows, H]    fp32 out, or NULL
+ * D = 128, 1 <= H <= 128.  rows = 0 is a no-op.  Asynchronous on stream.
+ */
+si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_t H, int32_t D,
+                             void* q8, float* w_eff, float* q_scale, void* stream);
+
+/*
  * si_materialize_scores -- reference path, score write-out.  Writes the head-summed
  * scores of query rows [row0, row0 + rows) for every batch entry into
  * scores [B, rows, T] fp32, -inf where the key is masked.  Same arithmetic, bit for
@@ -206,7 +241,7 @@ si_status si_indexer_merge_chunk(int64_t B, int64_t S, int64_t T, int32_t H, int
  * abstract.)  0 <= row0, row0 + rows <= S.
  */
 si_status si_materialize_scores(const void* q, si_dtype q_dtype,
-                                const void* kc, si_dtype kc_dtype, const float* kc_scale,
+                                const void* kc, si_dtype kc_dtype, const void* kc_scale,
                                 const float* w,
                                 int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                                 int32_t m, int64_t q_pos0, int64_t row0, int64_t rows,
@@ -221,7 +256,7 @@ si_status si_materialize_scores(const void* q, si_dtype q_dtype,
  * scores_ws: device buffer of at least B * row_block * T * 4 bytes.
  */
 si_status si_materialize_topk(const void* q, si_dtype q_dtype,
-                              const void* kc, si_dtype kc_dtype, const float* kc_scale,
+                              const void* kc, si_dtype kc_dtype, const void* kc_scale,
                               const float* w,
                               int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                               int32_t m, int32_t k, int64_t q_pos0,

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     materialize_scores,
     materialize_topk,
     plan,
+    quantize_q,
     workspace,
     workspace_bytes,
 )
@@ -23,5 +24,5 @@ _lib.load()
 
 __all__ = [
     "Plan", "SiError", "indexer_topk", "indexer_select_chunk", "indexer_merge_chunk",
-    "materialize_scores", "materialize_topk", "plan", "workspace", "workspace_bytes",
+    "materialize_scores", "materialize_topk", "plan", "quantize_q", "workspace", "workspace_bytes",
 ]

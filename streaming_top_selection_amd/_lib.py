@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsi_indexer.so")
 
 SI_OK, SI_ERR_INVALID_ARG, SI_ERR_UNSUPPORTED, SI_ERR_WORKSPACE, SI_ERR_HIP = range(5)
-SI_BF16, SI_FP8_E4M3FN = 1, 2
+SI_BF16, SI_FP8_E4M3FN, SI_MXFP4_E2M1 = 1, 2, 3
 SI_NOALLOC_SCRATCH_BYTES = 256 << 20      # include/si_indexer.h
 
 
@@ -49,6 +49,7 @@ SIGNATURES = {
                                        _i32, _i32, _i64, _cfgp, _i32, _p, _sz, _p]),
     "si_indexer_merge_chunk": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _cfgp,
                                       _i32, _p, _p, _p, _sz, _p]),
+    "si_quantize_q_e4m3": (_i32, [_p, _p, _i64, _i32, _i32, _p, _p, _p, _p]),
     "si_materialize_scores": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32,
                                      _i32, _i64, _i64, _i64, _p, _p]),
     "si_materialize_topk": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,

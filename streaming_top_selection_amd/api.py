@@ -15,8 +15,7 @@ import torch
 
 from . import _lib
 
-_KC_DTYPES = {torch.bfloat16: _lib.SI_BF16, torch.uint8: _lib.SI_FP8_E4M3FN,
-              torch.float8_e4m3fn: _lib.SI_FP8_E4M3FN}
+_DTYPE_NAMES = {"bf16": _lib.SI_BF16, "e4m3fn": _lib.SI_FP8_E4M3FN, "mxfp4": _lib.SI_MXFP4_E2M1}
 
 
 @dataclass(frozen=True)
@@ -42,29 +41,55 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _kc_dtype(kc: torch.Tensor) -> int:
-    try:
-        return _KC_DTYPES[kc.dtype]
-    except KeyError:
-        raise TypeError(f"kc must be bfloat16 or E4M3 bytes (uint8), not {kc.dtype}") from None
+def _q_dtype(q: torch.Tensor) -> int:
+    """bf16 q, or E4M3 bytes (uint8 or float8_e4m3fn) from quantize_q."""
+    if q.dtype == torch.bfloat16:
+        return _lib.SI_BF16
+    if q.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return _lib.SI_FP8_E4M3FN
+    raise TypeError(f"q must be bfloat16 or E4M3 bytes (uint8), not {q.dtype}")
 
 
-def _shapes(q, kc, w, kc_scale):
+def _kc_dtype(kc: torch.Tensor, D: int, kc_dtype=None) -> int:
+    """bf16 keys; uint8 keys of width D are E4M3 bytes, of width D/2 MXFP4 nibbles
+    (or name the format: kc_dtype = "bf16" | "e4m3fn" | "mxfp4")."""
+    if kc_dtype is not None:
+        return _DTYPE_NAMES[kc_dtype]
+    if kc.dtype == torch.bfloat16:
+        return _lib.SI_BF16
+    if kc.dtype == torch.float8_e4m3fn:
+        return _lib.SI_FP8_E4M3FN
+    if kc.dtype == torch.uint8:
+        return _lib.SI_MXFP4_E2M1 if kc.shape[-1] * 2 == D else _lib.SI_FP8_E4M3FN
+    raise TypeError(f"kc must be bfloat16, E4M3 bytes or MXFP4 bytes (uint8), not {kc.dtype}")
+
+
+def _shapes(q, kc, w, kc_scale, kc_dtype=None):
+    """Checks shapes, dtypes and placement; returns (B, S, T, H, D, q dtype, key dtype)."""
     if q.dim() != 4 or kc.dim() != 3 or w.dim() != 3:
-        raise ValueError("expected q [B,S,H,D], kc [B,T,D], w [B,S,H]")
+        raise ValueError("expected q [B,S,H,D], kc [B,T,D] (MXFP4: [B,T,D/2]), w [B,S,H]")
     B, S, H, D = q.shape
     T = kc.shape[1]
-    if kc.shape[0] != B or kc.shape[2] != D or tuple(w.shape) != (B, S, H):
+    qd = _q_dtype(q)
+    kd = _kc_dtype(kc, D, kc_dtype)
+    width = D // 2 if kd == _lib.SI_MXFP4_E2M1 else D
+    if kc.shape[0] != B or kc.shape[2] != width or tuple(w.shape) != (B, S, H):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kc {tuple(kc.shape)}, w {tuple(w.shape)}")
-    if q.dtype != torch.bfloat16 or w.dtype != torch.float32:
-        raise TypeError("q must be bfloat16 and w float32")
-    _kc_dtype(kc)
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
     for name, t in (("q", q), ("kc", kc), ("w", w), ("kc_scale", kc_scale)):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if kc_scale is not None and (kc_scale.dtype != torch.float32 or tuple(kc_scale.shape) != (B, T)):
-        raise ValueError("kc_scale must be float32 [B, T]")
-    return B, S, T, H, D
+    if kd == _lib.SI_FP8_E4M3FN and kc_scale is not None and (
+            kc_scale.dtype != torch.float32 or tuple(kc_scale.shape) != (B, T)):
+        raise ValueError("E4M3 keys: kc_scale must be float32 [B, T]")
+    if kd == _lib.SI_MXFP4_E2M1 and kc_scale is not None and (
+            kc_scale.dtype != torch.uint8 or tuple(kc_scale.shape) != (B, T, D // 32)):
+        raise ValueError("MXFP4 keys: kc_scale must be uint8 E8M0 [B, T, D/32]")
+    return B, S, T, H, D, qd, kd
+
+
+_DTYPE_BY_CODE = {v: k for k, v in _DTYPE_NAMES.items()}
 
 
 def plan(B, S, T, H=64, D=128, m=4, k=512, q_pos0=0, kc_dtype="bf16", key_tile=0,
@@ -72,7 +97,7 @@ def plan(B, S, T, H=64, D=128, m=4, k=512, q_pos0=0, kc_dtype="bf16", key_tile=0
     """The driver's plan for a problem (host only, no device needed)."""
     lib = _lib.load()
     out = _lib.SiPlan()
-    dt = _lib.SI_BF16 if kc_dtype == "bf16" else _lib.SI_FP8_E4M3FN
+    dt = _DTYPE_NAMES[kc_dtype]
     cfg = _cfg(key_tile, query_chunk, key_partition)
     _lib.check(lib.si_indexer_plan(B, S, T, H, D, m, k, q_pos0, dt, ctypes.byref(cfg),
                                    ctypes.byref(out)))
@@ -98,13 +123,13 @@ def workspace(pl: Plan, device) -> torch.Tensor:
 
 def indexer_topk(q, kc, w, m: int, k: int, *, kc_scale=None, q_pos0: int = 0,
                  key_tile: int = 0, query_chunk: int = 0, key_partition: int = 0,
-                 out=None, ws=None):
+                 out=None, ws=None, kc_dtype=None):
     """Top-k compressed keys per query row (streaming path).  Returns (idx int32
-    [B,S,k], score float32 [B,S,k]) sorted by (score desc, idx asc), -1/-inf padded."""
-    B, S, T, H, D = _shapes(q, kc, w, kc_scale)
-    kcd = _kc_dtype(kc)
-    pl = plan(B, S, T, H, D, m, k, q_pos0, "bf16" if kcd == _lib.SI_BF16 else "e4m3fn",
-              key_tile, query_chunk, key_partition)
+    [B,S,k], score float32 [B,S,k]) sorted by (score desc, idx asc), -1/-inf padded.
+    q is bf16, or E4M3 bytes from quantize_q with w its effective weights."""
+    B, S, T, H, D, qd, kcd = _shapes(q, kc, w, kc_scale, kc_dtype)
+    pl = plan(B, S, T, H, D, m, k, q_pos0, _DTYPE_BY_CODE[kcd], key_tile, query_chunk,
+              key_partition)
     if out is None:
         out = (torch.empty((B, S, k), dtype=torch.int32, device=q.device),
                torch.empty((B, S, k), dtype=torch.float32, device=q.device))
@@ -113,20 +138,20 @@ def indexer_topk(q, kc, w, m: int, k: int, *, kc_scale=None, q_pos0: int = 0,
     cfg = _cfg(key_tile, query_chunk, key_partition)
     lib = _lib.load()
     _lib.check(lib.si_indexer_topk(
-        _ptr(q), _lib.SI_BF16, _ptr(kc), kcd, _ptr(kc_scale), _ptr(w), B, S, T, H, D, m, k,
+        _ptr(q), qd, _ptr(kc), kcd, _ptr(kc_scale), _ptr(w), B, S, T, H, D, m, k,
         q_pos0, ctypes.byref(cfg), _ptr(out[0]), _ptr(out[1]), _ptr(ws), ws.numel(),
         _stream(q.device)))
     return out
 
 
 def indexer_select_chunk(q, kc, w, m, k, chunk, ws, *, kc_scale=None, q_pos0=0,
-                         key_tile=0, query_chunk=0, key_partition=0):
+                         key_tile=0, query_chunk=0, key_partition=0, kc_dtype=None):
     """Select stage of one query chunk (fused scoring + local top-k into ws)."""
-    B, S, T, H, D = _shapes(q, kc, w, kc_scale)
+    B, S, T, H, D, qd, kcd = _shapes(q, kc, w, kc_scale, kc_dtype)
     cfg = _cfg(key_tile, query_chunk, key_partition)
     lib = _lib.load()
     _lib.check(lib.si_indexer_select_chunk(
-        _ptr(q), _lib.SI_BF16, _ptr(kc), _kc_dtype(kc), _ptr(kc_scale), _ptr(w), B, S, T, H, D,
+        _ptr(q), qd, _ptr(kc), kcd, _ptr(kc_scale), _ptr(w), B, S, T, H, D,
         m, k, q_pos0, ctypes.byref(cfg), chunk, _ptr(ws), ws.numel(), _stream(q.device)))
 
 
@@ -134,30 +159,31 @@ def indexer_merge_chunk(B, S, T, H, D, m, k, chunk, ws, out, *, q_pos0=0, kc_dty
                         key_tile=0, query_chunk=0, key_partition=0):
     """Merge stage of one query chunk (partition lists in ws -> rows of out)."""
     cfg = _cfg(key_tile, query_chunk, key_partition)
-    dt = _lib.SI_BF16 if kc_dtype == "bf16" else _lib.SI_FP8_E4M3FN
+    dt = _DTYPE_NAMES[kc_dtype]
     lib = _lib.load()
     _lib.check(lib.si_indexer_merge_chunk(
         B, S, T, H, D, m, k, q_pos0, dt, ctypes.byref(cfg), chunk, _ptr(out[0]), _ptr(out[1]),
         _ptr(ws), ws.numel(), _stream(ws.device)))
 
 
-def materialize_scores(q, kc, w, m, *, kc_scale=None, q_pos0=0, row0=0, rows=None, out=None):
+def materialize_scores(q, kc, w, m, *, kc_scale=None, q_pos0=0, row0=0, rows=None, out=None,
+                       kc_dtype=None):
     """Head-summed scores [B, rows, T] fp32 (-inf where masked), reference path."""
-    B, S, T, H, D = _shapes(q, kc, w, kc_scale)
+    B, S, T, H, D, qd, kcd = _shapes(q, kc, w, kc_scale, kc_dtype)
     rows = S - row0 if rows is None else rows
     if out is None:
         out = torch.empty((B, rows, T), dtype=torch.float32, device=q.device)
     lib = _lib.load()
     _lib.check(lib.si_materialize_scores(
-        _ptr(q), _lib.SI_BF16, _ptr(kc), _kc_dtype(kc), _ptr(kc_scale), _ptr(w), B, S, T, H, D,
+        _ptr(q), qd, _ptr(kc), kcd, _ptr(kc_scale), _ptr(w), B, S, T, H, D,
         m, q_pos0, row0, rows, _ptr(out), _stream(q.device)))
     return out
 
 
 def materialize_topk(q, kc, w, m, k, *, kc_scale=None, q_pos0=0, row_block=None, out=None,
-                     scores_ws=None):
+                     scores_ws=None, kc_dtype=None):
     """Materialise-then-select reference path; same output contract as indexer_topk."""
-    B, S, T, H, D = _shapes(q, kc, w, kc_scale)
+    B, S, T, H, D, qd, kcd = _shapes(q, kc, w, kc_scale, kc_dtype)
     row_block = max(1, min(S, 4096)) if row_block is None else row_block
     if out is None:
         out = (torch.empty((B, S, k), dtype=torch.int32, device=q.device),
@@ -167,7 +193,29 @@ def materialize_topk(q, kc, w, m, k, *, kc_scale=None, q_pos0=0, row_block=None,
                                 device=q.device)
     lib = _lib.load()
     _lib.check(lib.si_materialize_topk(
-        _ptr(q), _lib.SI_BF16, _ptr(kc), _kc_dtype(kc), _ptr(kc_scale), _ptr(w), B, S, T, H, D,
+        _ptr(q), qd, _ptr(kc), kcd, _ptr(kc_scale), _ptr(w), B, S, T, H, D,
         m, k, q_pos0, _ptr(out[0]), _ptr(out[1]), _ptr(scores_ws), scores_ws.numel() * 4,
         row_block, _stream(q.device)))
     return out
+
+
+def quantize_q(q, w, *, out=None, with_scale=False):
+    """si_quantize_q_e4m3: per-(row, head) E4M3 q and the effective weights w * scale.
+    q bf16 [B, S, H, D], w float32 [B, S, H].  Returns (q8 uint8 [B, S, H, D], w_eff
+    float32 [B, S, H]) and, with with_scale, the scales [B, S, H] as a third item."""
+    if q.dim() != 4 or w.dim() != 3 or tuple(w.shape) != tuple(q.shape[:3]):
+        raise ValueError("expected q [B,S,H,D] and w [B,S,H]")
+    if q.dtype != torch.bfloat16 or w.dtype != torch.float32:
+        raise TypeError("q must be bfloat16 and w float32")
+    for name, t in (("q", q), ("w", w)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, S, H, D = q.shape
+    if out is None:
+        out = (torch.empty((B, S, H, D), dtype=torch.uint8, device=q.device),
+               torch.empty((B, S, H), dtype=torch.float32, device=q.device))
+    scale = torch.empty((B, S, H), dtype=torch.float32, device=q.device) if with_scale else None
+    lib = _lib.load()
+    _lib.check(lib.si_quantize_q_e4m3(_ptr(q), _ptr(w), B * S, H, D, _ptr(out[0]), _ptr(out[1]),
+                                      _ptr(scale), _stream(q.device)))
+    return (*out, scale) if with_scale else out

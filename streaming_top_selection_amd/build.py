@@ -3,8 +3,9 @@
     python streaming_top_selection_amd/build.py   (run by path: importing the package
                                                   loads the library it builds)
 
-Every ``csrc/*.hip`` source is compiled with hipcc to an object in parallel, then the
-objects are linked into ``streaming_top_selection_amd/libsi_indexer.so``.
+Every ``csrc/*.hip`` source is compiled with hipcc to an object in parallel (the
+select kernel's instantiation file once per register-tile shape and operand mode),
+then the objects are linked into ``streaming_top_selection_amd/libsi_indexer.so``.
 """
 
 from __future__ import annotations
@@ -50,22 +51,44 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+# Select kernel register-tile shapes (waves, key blocks per wave, register tiles per key
+# tile), one per key tile 64, 128, 256, 512, 768, 1024 (the plan's table), and the
+# operand modes (bf16 x bf16, bf16 x E4M3, E4M3 x E4M3, E4M3 x MXFP4).  Each pair is
+# its own object of si_select_inst.hip.
+SELECT_SHAPES = [(2, 1, 1), (4, 1, 1), (4, 2, 1), (4, 4, 1), (4, 2, 3), (4, 4, 2)]
+SELECT_OPS = [0, 1, 2, 3]
+SELECT_INST = "si_select_inst.hip"
+
+
+def _compile(job) -> str:
+    src, defs, tag = job
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + tag + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *defs, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {src} {defs}:\n{r.stdout}\n{r.stderr}")
     return obj
+
+
+def jobs_list():
+    """(source, -D flags, object tag) of every object of the library."""
+    out = []
+    for nw, kb, ns in SELECT_SHAPES:
+        for op in SELECT_OPS:
+            out.append((os.path.join(CSRC, SELECT_INST),
+                        [f"-DSI_NW={nw}", f"-DSI_KB={kb}", f"-DSI_NS={ns}", f"-DSI_OP={op}"],
+                        f".{nw}_{kb}_{ns}_op{op}"))
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        if os.path.basename(src) != SELECT_INST:
+            out.append((src, [], ""))
+    # the largest units (four key blocks per wave) first, so the pool stays busy
+    return sorted(out, key=lambda j: (not any(d in ("-DSI_KB=4",) for d in j[1]), j[2]))
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    # the largest units (the KB = 4 select kernels) first, so the pool stays busy
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")),
-                     key=lambda f: (not ("kt512" in f or "kt1024" in f), f))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, sources))
+        objs = list(ex.map(_compile, jobs_list()))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -35,10 +35,10 @@ si_status hip_fail(hipError_t e, const char* where) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-si::Problem make_problem(const void* q, const void* kc, const float* kc_scale, const float* w,
+si::Problem make_problem(const void* q, const void* kc, const void* kc_scale, const float* w,
                          int64_t B, int64_t S, int64_t T, int32_t H, int32_t m, int64_t q_pos0) {
     si::Problem P;
-    P.q = static_cast<const uint16_t*>(q);
+    P.q = q;
     P.kc = kc;
     P.kc_scale = kc_scale;
     P.w = w;
@@ -51,17 +51,33 @@ si::Problem make_problem(const void* q, const void* kc, const float* kc_scale, c
     return P;
 }
 
+// The score tile's operand mode for a (q, keys) dtype pair, or -1 if not built.
+int operand_mode(si_dtype q_dtype, si_dtype kc_dtype) {
+    if (q_dtype == SI_BF16 && kc_dtype == SI_BF16) return si::kOpBf16;
+    if (q_dtype == SI_BF16 && kc_dtype == SI_FP8_E4M3FN) return si::kOpBf16K8;
+    if (q_dtype == SI_FP8_E4M3FN && kc_dtype == SI_FP8_E4M3FN) return si::kOpF8;
+    if (q_dtype == SI_FP8_E4M3FN && kc_dtype == SI_MXFP4_E2M1) return si::kOpF8K4;
+    return -1;
+}
+
 // Pointer and dtype checks for the inputs of every scoring entry point.  A tensor
 // with no elements may have a NULL pointer.
 si_status check_inputs(const void* q, si_dtype q_dtype, const void* kc, si_dtype kc_dtype,
-                       const float* kc_scale, const float* w, int64_t B, int64_t S,
+                       const void* kc_scale, const float* w, int64_t B, int64_t S,
                        int64_t T) {
     const bool rows = B > 0 && S > 0, keys = B > 0 && T > 0;
-    if (q_dtype != SI_BF16) return fail(SI_ERR_UNSUPPORTED, "q must be SI_BF16");
+    if (q_dtype != SI_BF16 && q_dtype != SI_FP8_E4M3FN)
+        return fail(SI_ERR_UNSUPPORTED, "q must be SI_BF16 or SI_FP8_E4M3FN");
+    if (operand_mode(q_dtype, kc_dtype) < 0)
+        return fail(SI_ERR_UNSUPPORTED,
+                    q_dtype == SI_BF16 ? "bf16 q takes bf16 or E4M3 keys (MXFP4 keys need E4M3 q)"
+                                       : "E4M3 q takes E4M3 or MXFP4 keys");
     if ((rows && (!q || !w)) || (keys && !kc))
         return fail(SI_ERR_INVALID_ARG, "q, kc and w must not be NULL");
     if (kc_dtype == SI_FP8_E4M3FN && keys && !kc_scale)
         return fail(SI_ERR_INVALID_ARG, "E4M3 keys need kc_scale");
+    if (kc_dtype == SI_MXFP4_E2M1 && keys && !kc_scale)
+        return fail(SI_ERR_INVALID_ARG, "MXFP4 keys need their E8M0 block scales in kc_scale");
     if (kc_dtype == SI_BF16 && kc_scale)
         return fail(SI_ERR_INVALID_ARG, "kc_scale must be NULL for bf16 keys");
     if ((rows && (!aligned(q, 16) || !aligned(w, 4))) || (keys && !aligned(kc, 16)) ||
@@ -88,7 +104,7 @@ si_status check_workspace(const si::PlanInternal& pl, const void* ws, size_t ws_
 }
 
 si_status run_select(const si::PlanInternal& pl, const si::Problem& P, int32_t k,
-                     int32_t chunk, void* ws, bool fp8, hipStream_t stream) {
+                     int32_t chunk, void* ws, int op, hipStream_t stream) {
     const int64_t qc = pl.pub.query_chunk;
     si::SelectArgs a;
     a.P = P;
@@ -103,7 +119,7 @@ si_status run_select(const si::PlanInternal& pl, const si::Problem& P, int32_t k
     a.cand = static_cast<uint64_t*>(ws);
     a.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.cand_bytes);
     const hipError_t e = si::launch_select(a, pl.nwave, pl.kb, pl.nsub, pl.pub.cand_capacity,
-                                           fp8, stream);
+                                           op, stream);
     if (e != hipSuccess) return hip_fail(e, "select kernel launch");
     return SI_OK;
 }
@@ -198,7 +214,7 @@ size_t si_indexer_topk_workspace_bytes(int64_t B, int64_t S, int64_t T, int32_t 
 }
 
 si_status si_indexer_select_chunk(const void* q, si_dtype q_dtype, const void* kc,
-                                  si_dtype kc_dtype, const float* kc_scale, const float* w,
+                                  si_dtype kc_dtype, const void* kc_scale, const float* w,
                                   int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                                   int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
                                   int32_t chunk, void* workspace, size_t workspace_bytes,
@@ -214,7 +230,7 @@ si_status si_indexer_select_chunk(const void* q, si_dtype q_dtype, const void* k
         return fail(SI_ERR_INVALID_ARG, "chunk out of range");
     }
     const si::Problem P = make_problem(q, kc, kc_scale, w, B, S, T, H, m, q_pos0);
-    return run_select(pl, P, k, chunk, workspace, kc_dtype == SI_FP8_E4M3FN,
+    return run_select(pl, P, k, chunk, workspace, operand_mode(q_dtype, kc_dtype),
                       static_cast<hipStream_t>(stream));
 }
 
@@ -239,7 +255,7 @@ si_status si_indexer_merge_chunk(int64_t B, int64_t S, int64_t T, int32_t H, int
 }
 
 si_status si_indexer_topk(const void* q, si_dtype q_dtype, const void* kc, si_dtype kc_dtype,
-                          const float* kc_scale, const float* w, int64_t B, int64_t S,
+                          const void* kc_scale, const float* w, int64_t B, int64_t S,
                           int64_t T, int32_t H, int32_t D, int32_t m, int32_t k,
                           int64_t q_pos0, const si_config* cfg, int32_t* out_idx,
                           float* out_score, void* workspace, size_t workspace_bytes,
@@ -255,7 +271,8 @@ si_status si_indexer_topk(const void* q, si_dtype q_dtype, const void* kc, si_dt
     const si::Problem P = make_problem(q, kc, kc_scale, w, B, S, T, H, m, q_pos0);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t c = 0; c < pl.pub.n_chunks; ++c) {
-        if ((st = run_select(pl, P, k, c, workspace, kc_dtype == SI_FP8_E4M3FN, s)) != SI_OK)
+        if ((st = run_select(pl, P, k, c, workspace, operand_mode(q_dtype, kc_dtype), s)) !=
+            SI_OK)
             return st;
         if ((st = run_merge(pl, B, S, T, m, k, q_pos0, c, out_idx, out_score, workspace, s)) !=
             SI_OK)
@@ -265,7 +282,7 @@ si_status si_indexer_topk(const void* q, si_dtype q_dtype, const void* kc, si_dt
 }
 
 si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype, const void* kc,
-                                  si_dtype kc_dtype, const float* kc_scale, const float* w,
+                                  si_dtype kc_dtype, const void* kc_scale, const float* w,
                                   int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                                   int32_t m, int32_t k, int64_t q_pos0, const si_config* cfg,
                                   int32_t* out_idx, float* out_score, void* stream) {
@@ -294,15 +311,40 @@ si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype, const void* k
     const si::Problem P = make_problem(q, kc, kc_scale, w, B, S, T, H, m, q_pos0);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t c = 0; c < pl.pub.n_chunks; ++c) {
-        if ((st = run_select(pl, P, k, c, ws, kc_dtype == SI_FP8_E4M3FN, s)) != SI_OK) return st;
+        if ((st = run_select(pl, P, k, c, ws, operand_mode(q_dtype, kc_dtype), s)) != SI_OK)
+            return st;
         if ((st = run_merge(pl, B, S, T, m, k, q_pos0, c, out_idx, out_score, ws, s)) != SI_OK)
             return st;
     }
     return SI_OK;
 }
 
+si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_t H, int32_t D,
+                             void* q8, float* w_eff, float* q_scale, void* stream) {
+    g_last_error.clear();
+    if (rows < 0) return fail(SI_ERR_INVALID_ARG, "rows must be >= 0");
+    if (H < 1 || D < 1) return fail(SI_ERR_INVALID_ARG, "H and D must be >= 1");
+    if (D != si::kPlanD) return fail(SI_ERR_UNSUPPORTED, "only D = 128 is built");
+    if (H > si::kPlanMaxH) return fail(SI_ERR_UNSUPPORTED, "H must be <= 128");
+    if (rows == 0) return SI_OK;
+    if (!q || !w || !q8 || !w_eff) return fail(SI_ERR_INVALID_ARG, "q, w, q8 and w_eff must not be NULL");
+    if (!aligned(q, 8) || !aligned(q8, 4) || !aligned(w, 4) || !aligned(w_eff, 4) ||
+        (q_scale && !aligned(q_scale, 4)))
+        return fail(SI_ERR_INVALID_ARG, "q must be 8-byte aligned, q8, w, w_eff and q_scale 4-byte");
+    si::QuantArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.w = w;
+    a.q8 = static_cast<uint8_t*>(q8);
+    a.w_eff = w_eff;
+    a.q_scale = q_scale;
+    a.nvec = rows * H;
+    const hipError_t e = si::launch_quantize_q(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "quantize kernel launch");
+    return SI_OK;
+}
+
 si_status si_materialize_scores(const void* q, si_dtype q_dtype, const void* kc,
-                                si_dtype kc_dtype, const float* kc_scale, const float* w,
+                                si_dtype kc_dtype, const void* kc_scale, const float* w,
                                 int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
                                 int32_t m, int64_t q_pos0, int64_t row0, int64_t rows,
                                 float* scores, void* stream) {
@@ -323,14 +365,14 @@ si_status si_materialize_scores(const void* q, si_dtype q_dtype, const void* kc,
     a.n_row_tiles = (int32_t)si::ceil_div(row0 + rows - a.tile_row0, si::kPlanTQ);
     a.n_key_tiles = (int32_t)si::ceil_div(T, 512);
     a.scores = scores;
-    const hipError_t e = si::launch_mat_score(a, kc_dtype == SI_FP8_E4M3FN,
+    const hipError_t e = si::launch_mat_score(a, operand_mode(q_dtype, kc_dtype),
                                               static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "materialise score kernel launch");
     return SI_OK;
 }
 
 si_status si_materialize_topk(const void* q, si_dtype q_dtype, const void* kc, si_dtype kc_dtype,
-                              const float* kc_scale, const float* w, int64_t B, int64_t S,
+                              const void* kc_scale, const float* w, int64_t B, int64_t S,
                               int64_t T, int32_t H, int32_t D, int32_t m, int32_t k,
                               int64_t q_pos0, int32_t* out_idx, float* out_score,
                               float* scores_ws, size_t scores_ws_bytes, int64_t row_block,

@@ -58,13 +58,26 @@ struct MatSelectArgs {
     float* out_score;
 };
 
-hipError_t launch_select(const SelectArgs& a, int nwave, int kb, int nsub, int cg, bool fp8,
+// E4M3 quantisation of q vectors (rows x heads vectors of kD bf16).
+struct QuantArgs {
+    const uint16_t* q;     // [nvec, kD] bf16 bits
+    const float* w;        // [nvec] head weights
+    uint8_t* q8;           // [nvec, kD] E4M3 bytes
+    float* w_eff;          // [nvec] w * scale
+    float* q_scale;        // [nvec] scale, or null
+    int64_t nvec;
+};
+
+hipError_t launch_quantize_q(const QuantArgs& a, hipStream_t stream);
+
+// op: operand mode (kOpBf16 .. kOpF8K4, si_score.hpp)
+hipError_t launch_select(const SelectArgs& a, int nwave, int kb, int nsub, int cg, int op,
                          hipStream_t stream);
 // one register-tile shape (NWAVE waves x KB blocks x NSUB register tiles per key tile)
-template <int NWAVE, int KB, int NSUB, bool FP8>
+template <int NWAVE, int KB, int NSUB, int OP>
 hipError_t launch_select_shape(const SelectArgs& a, int cg, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
-hipError_t launch_mat_score(const MatScoreArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_mat_score(const MatScoreArgs& a, int op, hipStream_t stream);
 hipError_t launch_mat_select(const MatSelectArgs& a, hipStream_t stream);
 
 }  // namespace si

@@ -5,16 +5,17 @@
 // on the score values, an index-order pass that takes the lowest indices among
 // scores equal to the k-th, and a rank sort.
 #include "si_kernels.hpp"
+#include "si_score_q8.hpp"
 
 namespace si {
 
 // ---- score write-out: one workgroup = 32 rows x 512 keys --------------------------
-template <bool FP8>
+template <int OP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mat_score_kernel(MatScoreArgs A) {
     constexpr int NWAVE = 4, KB = 4, RT = NWAVE * KB * kMB;
     __shared__ ScoreLds L;
-    SI_DECLARE_QBUFS(Q);
+    SI_DECLARE_QBUFS(Q, OP);
     const Problem& P = A.P;
     const int lane = threadIdx.x & 63, wave = wave_id();
 
@@ -33,7 +34,7 @@ mat_score_kernel(MatScoreArgs A) {
     if (live) {
         load_w_tile<NWAVE * 64>(P, b, trow0, rows_valid, L);
         __syncthreads();
-        score_regs<NWAVE, KB, FP8>(P, b, trow0, rows_valid, key0, P.T, L, Q, acc);
+        score_tile<NWAVE, KB, OP>(P, b, trow0, rows_valid, key0, P.T, L, Q, acc);
     }
     // register r holds row trow0 + mfma_row(r, lane); lanes run along the keys, so
     // each store writes 32 consecutive scores of two rows
@@ -134,13 +135,25 @@ __global__ void __launch_bounds__(64) mat_select_kernel(MatSelectArgs A) {
     }
 }
 
-hipError_t launch_mat_score(const MatScoreArgs& a, bool fp8, hipStream_t stream) {
+hipError_t launch_mat_score(const MatScoreArgs& a, int op, hipStream_t stream) {
     const int64_t grid = (int64_t)a.n_row_tiles * a.n_key_tiles * a.P.B;
     if (grid <= 0) return hipSuccess;
-    if (fp8)
-        hipLaunchKernelGGL(mat_score_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(mat_score_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    switch (op) {
+        case kOpBf16:
+            hipLaunchKernelGGL(mat_score_kernel<kOpBf16>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+            break;
+        case kOpBf16K8:
+            hipLaunchKernelGGL(mat_score_kernel<kOpBf16K8>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+            break;
+        case kOpF8:
+            hipLaunchKernelGGL(mat_score_kernel<kOpF8>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+            break;
+        case kOpF8K4:
+            hipLaunchKernelGGL(mat_score_kernel<kOpF8K4>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -46,8 +46,8 @@ inline si_status check_shape(int64_t B, int64_t S, int64_t T, int32_t H, int32_t
     if (D != kPlanD) { msg = "only D = 128 is built"; return SI_ERR_UNSUPPORTED; }
     if (H > kPlanMaxH) { msg = "H must be <= 128"; return SI_ERR_UNSUPPORTED; }
     if (T >= int64_t(0x7FFFFFFF)) { msg = "T must be < 2^31 - 1"; return SI_ERR_UNSUPPORTED; }
-    if (kc_dtype != SI_BF16 && kc_dtype != SI_FP8_E4M3FN) {
-        msg = "key dtype must be SI_BF16 or SI_FP8_E4M3FN"; return SI_ERR_UNSUPPORTED;
+    if (kc_dtype != SI_BF16 && kc_dtype != SI_FP8_E4M3FN && kc_dtype != SI_MXFP4_E2M1) {
+        msg = "key dtype must be SI_BF16, SI_FP8_E4M3FN or SI_MXFP4_E2M1"; return SI_ERR_UNSUPPORTED;
     }
     if (S > (int64_t(1) << 40) || B > (int64_t(1) << 20)) {
         msg = "B or S too large"; return SI_ERR_UNSUPPORTED;

@@ -35,14 +35,26 @@
 namespace si {
 
 struct Problem {
-    const uint16_t* q;        // [B, S, H, D] bf16 bits
-    const void* kc;           // [B, T, D] bf16 bits or E4M3 bytes
-    const float* kc_scale;    // [B, T] (E4M3 keys) or nullptr
-    const float* w;           // [B, S, H]
+    const void* q;            // [B, S, H, D] bf16 bits or E4M3 bytes
+    const void* kc;           // [B, T, D] bf16 bits or E4M3 bytes, [B, T, D/2] MXFP4 nibbles
+    const void* kc_scale;     // [B, T] fp32 (E4M3 keys), [B, T, D/32] E8M0 (MXFP4), or null
+    const float* w;           // [B, S, H] head weights (E4M3 q: the effective w * q_scale)
     int64_t B, S, T;
     int32_t H, m;
     int64_t q_pos0;
 };
+
+// Operand modes of the score tile (q format x key format) and the MFMA they run on.
+enum : int {
+    kOpBf16 = 0,     // bf16 q x bf16 keys: v_mfma_f32_32x32x16_bf16
+    kOpBf16K8 = 1,   // bf16 q x E4M3 keys widened exactly to bf16: the same bf16 MFMA
+    kOpF8 = 2,       // E4M3 q x E4M3 keys: v_mfma_f32_32x32x64_f8f6f4
+    kOpF8K4 = 3      // E4M3 q x MXFP4 keys: v_mfma_scale_f32_32x32x64_f8f6f4, E8M0 scales
+};
+constexpr bool op_q8(int op) { return op >= kOpF8; }
+constexpr bool op_row_scale(int op) { return op == kOpBf16K8 || op == kOpF8; }
+// bytes of one staged q tile (32 rows x D elements of one head)
+constexpr int op_q_tile_bytes(int op) { return op_q8(op) ? kTQ * kD : kTQ * kD * 2; }
 
 constexpr int kQBuf = 8;             // q tiles in flight: head h+7 loads while h+1 is read
 constexpr int kWHeads = kMaxH + kQBuf;       // weight rows: H heads, then zeros
@@ -62,11 +74,11 @@ struct QBufs {
     uint16_t* p[kQBuf];
 };
 
-#define SI_DECLARE_QBUFS(name)                                                        \
-    __shared__ __attribute__((aligned(16))) uint16_t name##0[si::kQTile],            \
-        name##1[si::kQTile], name##2[si::kQTile], name##3[si::kQTile],               \
-        name##4[si::kQTile], name##5[si::kQTile], name##6[si::kQTile],               \
-        name##7[si::kQTile];                                                          \
+#define SI_DECLARE_QBUFS(name, OP)                                                    \
+    constexpr int name##_n = si::op_q_tile_bytes(OP) / 2;                             \
+    __shared__ __attribute__((aligned(16))) uint16_t name##0[name##_n],              \
+        name##1[name##_n], name##2[name##_n], name##3[name##_n], name##4[name##_n],  \
+        name##5[name##_n], name##6[name##_n], name##7[name##_n];                     \
     const si::QBufs name = {{name##0, name##1, name##2, name##3, name##4, name##5,   \
                              name##6, name##7}}
 
@@ -121,7 +133,7 @@ __device__ __forceinline__ void load_w_tile(const Problem& P, int64_t b, int64_t
 // key_end score as if zero: a caller that masks them anyway passes the end of what any
 // of its rows sees, and zero operands there cost the MFMAs less power.
 template <int NWAVE, int KB, bool FP8>
-__device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t row0,
+__device__ __forceinline__ void score_regs_bf16(const Problem& P, int64_t b, int64_t row0,
                                            int rows_valid, int64_t key0, int64_t key_end,
                                            ScoreLds& L, const QBufs& Q, f32x16 (&acc)[KB]) {
     constexpr int NT = NWAVE * kWave;
@@ -180,7 +192,8 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
     constexpr int QN = kQChunks / NT;
     static_assert(kQChunks % NT == 0, "every wave issues the same number of q loads");
     constexpr int AHEAD = kQBuf - 2;
-    const uint64_t qbase = reinterpret_cast<uint64_t>(P.q + (b * P.S + row0) * H * (int64_t)kD);
+    const uint64_t qbase = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(P.q) +
+                                                      (b * P.S + row0) * H * (int64_t)kD);
     const uint32_t qbytes = (uint32_t)(rows_valid * H * kD * 2);
     int voff[QN];
 #pragma unroll
@@ -354,7 +367,7 @@ __device__ __forceinline__ void score_regs(const Problem& P, int64_t b, int64_t 
         kscale[kb] = 1.0f;
         if constexpr (FP8) {
             const int64_t key = key0 + (int64_t)(wave * KB + kb) * kMB + il;
-            if (key < P.T) kscale[kb] = P.kc_scale[b * P.T + key];
+            if (key < P.T) kscale[kb] = static_cast<const float*>(P.kc_scale)[b * P.T + key];
         }
     }
 

@@ -30,6 +30,7 @@
 
 #include "si_compact.hpp"
 #include "si_kernels.hpp"
+#include "si_score_q8.hpp"
 
 namespace si {
 
@@ -167,7 +168,7 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
 }
 
 // One wave per SIMD (512 registers each): see score_regs.
-template <int NWAVE, int KB, int NSUB, int CG, bool FP8>
+template <int NWAVE, int KB, int NSUB, int CG, int OP>
 __global__ void __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 select_kernel(SelectArgs A) {
     constexpr int NT = NWAVE * 64;
@@ -177,7 +178,7 @@ select_kernel(SelectArgs A) {
     static_assert(CG % 64 == 0, "capacity must be a multiple of the wave size");
 
     __shared__ ScoreLds L;
-    SI_DECLARE_QBUFS(Q);
+    SI_DECLARE_QBUFS(Q, OP);
     __shared__ float sThf[kTQ];            // threshold score (-inf: none; +inf: no row)
     __shared__ int32_t sCnt[kTQ];          // candidates in the query's buffer
     __shared__ int32_t sN[kTQ];            // end of the query's visible keys here
@@ -227,7 +228,7 @@ select_kernel(SelectArgs A) {
     int sub = 0;
     for (int64_t key0 = key_lo; key0 < key_hi; key0 += RT) {
         f32x16 acc[KB];
-        score_regs<NWAVE, KB, FP8>(P, b, row0, rows_valid, key0, key_hi, L, Q, acc);
+        score_tile<NWAVE, KB, OP>(P, b, row0, rows_valid, key0, key_hi, L, Q, acc);
 
         const int64_t kbase = key0 + (int64_t)wave * KB * kMB;
         uint64_t* const cand_tile = A.cand + slot0 * CGS;
@@ -264,22 +265,22 @@ select_kernel(SelectArgs A) {
     if (tid < rows_valid) A.cnt[slot0 + (int64_t)tid * A.P_ws] = min(sCnt[tid], A.k);
 }
 
-template <int NWAVE, int KB, int NSUB, int CG, bool FP8>
+template <int NWAVE, int KB, int NSUB, int CG, int OP>
 static hipError_t launch_one(const SelectArgs& a, hipStream_t stream) {
     const int64_t grid = (int64_t)a.n_tiles * a.P_chunk * a.P.B;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((select_kernel<NWAVE, KB, NSUB, CG, FP8>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((select_kernel<NWAVE, KB, NSUB, CG, OP>), dim3((unsigned)grid),
                        dim3(NWAVE * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-// Launches the select kernel of one register-tile shape for either candidate capacity.
-// Each shape is instantiated in a source file of its own (si_select_kt*.hip), so the
-// kernels compile in parallel.
-template <int NWAVE, int KB, int NSUB, bool FP8>
+// Launches the select kernel of one register-tile shape and operand mode for either
+// candidate capacity.  Each (shape, mode) is instantiated in an object of its own
+// (si_select_inst.hip, compiled once per pair), so the kernels compile in parallel.
+template <int NWAVE, int KB, int NSUB, int OP>
 hipError_t launch_select_shape(const SelectArgs& a, int cg, hipStream_t stream) {
-    if (cg == 2048) return launch_one<NWAVE, KB, NSUB, 2048, FP8>(a, stream);
-    if (cg == 4096) return launch_one<NWAVE, KB, NSUB, 4096, FP8>(a, stream);
+    if (cg == 2048) return launch_one<NWAVE, KB, NSUB, 2048, OP>(a, stream);
+    if (cg == 4096) return launch_one<NWAVE, KB, NSUB, 4096, OP>(a, stream);
     return hipErrorInvalidValue;
 }
 

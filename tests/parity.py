@@ -21,13 +21,14 @@ import oracle
 
 
 def check_rows(gidx, gscore, rows, q_bits, kc_bits, w, m, k, *, kc_dtype="bf16",
-               kc_scale=None, q_pos0=0, b=0, recall_gate=0.998, verbose=True):
+               kc_scale=None, q_pos0=0, b=0, recall_gate=0.998, verbose=True, q_dtype="bf16"):
     """gidx/gscore: [R, k] numpy GPU outputs for the query rows `rows` of batch b."""
     rows = list(rows)
     exact = oracle.score_rows(q_bits, kc_bits, w, m, kc_dtype=kc_dtype, kc_scale=kc_scale,
-                              q_pos0=q_pos0, rows=rows, b=b)
+                              q_pos0=q_pos0, rows=rows, b=b, q_dtype=q_dtype)
     beta = oracle.score_error_bound(q_bits, kc_bits, w, m, kc_dtype=kc_dtype,
-                                    kc_scale=kc_scale, q_pos0=q_pos0, rows=rows, b=b)
+                                    kc_scale=kc_scale, q_pos0=q_pos0, rows=rows, b=b,
+                                    q_dtype=q_dtype)
     T = exact.shape[1]
     recalls = []
     worst_rel = 0.0
@@ -78,14 +79,15 @@ def check_rows(gidx, gscore, rows, q_bits, kc_bits, w, m, k, *, kc_dtype="bf16",
 
 
 def check_score_block(gscores, rows, q_bits, kc_bits, w, m, *, kc_dtype="bf16", kc_scale=None,
-                      q_pos0=0, b=0):
+                      q_pos0=0, b=0, q_dtype="bf16"):
     """Element-by-element check of written scores [R, T]: -inf exactly where masked,
     within the fp32 error bound of the float64 score elsewhere."""
     rows = list(rows)
     exact = oracle.score_rows(q_bits, kc_bits, w, m, kc_dtype=kc_dtype, kc_scale=kc_scale,
-                              q_pos0=q_pos0, rows=rows, b=b)
+                              q_pos0=q_pos0, rows=rows, b=b, q_dtype=q_dtype)
     beta = oracle.score_error_bound(q_bits, kc_bits, w, m, kc_dtype=kc_dtype,
-                                    kc_scale=kc_scale, q_pos0=q_pos0, rows=rows, b=b)
+                                    kc_scale=kc_scale, q_pos0=q_pos0, rows=rows, b=b,
+                                    q_dtype=q_dtype)
     g = np.asarray(gscores, dtype=np.float64)
     masked = np.isneginf(exact)
     assert (np.isneginf(g) == masked).all(), "mask differs"

@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(si_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(si_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
