@@ -50,13 +50,19 @@ WORKLOADS = {
                      "D=128, top-k=512; q quantised per (row, head) to E4M3 inside the step, keys "
                      "MXFP4 (E2M1 + E8M0 per 32), scaled f8f6f4 MFMA",
 }
+WORKLOADS["long-two-stage"] = (
+    "Two-stage indexer at the long-context shape: B=1, S=262144, m=4, T=65536, H_I=64, D=128; "
+    "block keys = bf16 mean of 8 keys, coarse top-2048 blocks, fine top-512 of their keys "
+    "(+ the trailing incomplete block), bf16")
+TWO_STAGE = {"long-two-stage": dict(block=8, k_blocks=2048)}
 # workload -> input configuration (synth.CONFIGS); the fp8-q workloads quantise q in the step
-WORKLOAD_SPEC = {"v4flash-fp8": "v4flash-e4m3", "v4flash-mxfp4": "v4flash-mxfp4"}
+WORKLOAD_SPEC = {"v4flash-fp8": "v4flash-e4m3", "v4flash-mxfp4": "v4flash-mxfp4",
+                 "long-two-stage": "long"}
 FP8_Q = {"v4flash-fp8", "v4flash-mxfp4"}
 DTYPE_NAME = {("bf16", "bf16"): "bf16", ("bf16", "e4m3fn"): "bf16",
               ("e4m3fn", "e4m3fn"): "e4m3", ("e4m3fn", "mxfp4"): "e4m3xe2m1"}
 # default (steps, warmup) per workload: about a minute of timed work at most
-DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1)}
+DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1), "long-two-stage": (5, 1)}
 # q rows per slice of the million workload's streamed-q capacity pass
 CAPACITY_SLICE_ROWS = 16384
 
@@ -98,6 +104,117 @@ def visible_pairs(S, T, m, q_pos0=0):
     import numpy as np
     t = np.arange(q_pos0, q_pos0 + S, dtype=np.int64)
     return int(np.minimum(T, (t + 1) // m).sum())
+
+
+def two_stage_pairs(S, T, m, block, k_blocks, q_pos0=0):
+    """(coarse pairs, fine pairs) summed over rows: the complete visible blocks each
+    query scores, and its fine candidates (kept blocks' keys + trailing keys)."""
+    import numpy as np
+    t = np.arange(q_pos0, q_pos0 + S, dtype=np.int64)
+    n = np.minimum(T, (t + 1) // m)
+    nb = np.minimum(T // block, (t + 1) // (block * m))
+    fine = block * np.minimum(nb, k_blocks) + (n - block * nb)
+    return int(nb.sum()), int(fine.sum())
+
+
+def bench_two_stage(args, spec, dev):
+    """One step = block keys + the two-stage top-k over every query row (what
+    si_block_keys_mean + si_indexer_topk_two_stage enqueue), inputs resident."""
+    import numpy as np
+    import torch
+
+    import streaming_top_selection_amd as si
+    import synth
+    ts = TWO_STAGE[args.workload]
+    x = synth.make_inputs(spec, device=dev)
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    input_bytes = tensor_bytes(x["q"], x["kc"], x["w"])
+    kb = torch.empty((spec.B, spec.T // ts["block"], spec.D), dtype=torch.bfloat16, device=dev)
+    pl = si.two_stage_plan(spec.B, spec.S, spec.T, spec.H, spec.D, spec.m, spec.k,
+                           ts["k_blocks"], ts["block"], query_chunk=args.query_chunk)
+    ws = torch.empty(max(pl.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+    out = (torch.empty((spec.B, spec.S, spec.k), dtype=torch.int32, device=dev),
+           torch.empty((spec.B, spec.S, spec.k), dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        si.block_keys(x["kc"], ts["block"], out=kb)
+        si.indexer_topk_two_stage(x["q"], x["kc"], kb, x["w"], spec.m, spec.k,
+                                  k_blocks=ts["k_blocks"], block=ts["block"],
+                                  query_chunk=args.query_chunk, out=out, ws=ws)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    step_s = wall / args.steps
+    ev_s = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
+    peak = torch.cuda.max_memory_allocated(dev)
+    vis = spec.B * visible_pairs(spec.S, spec.T, spec.m)
+    cp, fp = two_stage_pairs(spec.S, spec.T, spec.m, ts["block"], ts["k_blocks"])
+    flops = spec.B * (cp + fp) * 2 * spec.H * spec.D
+    tflops = flops / ev_s / 1e12
+    rec = {
+        "metric": METRIC, "value": vis / step_s, "unit": "pairs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "B": spec.B, "S": spec.S, "T": spec.T,
+                   "H_I": spec.H, "D": spec.D, "m": spec.m, "k": spec.k,
+                   "block": ts["block"], "k_blocks": ts["k_blocks"],
+                   "query_chunk": pl.query_chunk, "n_chunks": pl.n_chunks},
+        "value_note": "value = causally visible (query, key) pairs of the single-stage problem "
+                      "per second; the two stages score scored_pairs of them",
+        "visible_pairs": vis,
+        "scored_pairs": {"coarse_block_pairs": spec.B * cp, "fine_candidate_pairs": spec.B * fp},
+        "peak_hbm_bytes": int(peak), "peak_hbm_gib": peak / 2 ** 30,
+        "hbm_bytes": {"inputs": input_bytes, "outputs": tensor_bytes(*out),
+                      "block_keys": tensor_bytes(kb), "workspace": int(ws.numel())},
+        "roofline": {
+            "kernel": "two-stage path (coarse select + merge, fine score, fine select; one call)",
+            "bound": "mfma", "achieved": tflops, "peak": BF16_DENSE_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tflops / BF16_DENSE_PEAK_TFLOPS, "traffic": None,
+            "mean_launch_ms": ev_s * 1e3, "flops_per_step": flops},
+    }
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        import oracle
+        rows = synth.sample_rows(spec.replace(k=8 * ts["k_blocks"]), 4096, salt=100)
+        rng = np.random.default_rng(100)
+        rng.shuffle(rows)
+        kcb = x["kc"][0:1].cpu().view(torch.int16).numpy().view(np.uint16)
+        done, pairs, hits = 0.0, 0, []
+        got = out[0][0].cpu().numpy()
+        while rows and done < args.cpu_seconds:
+            r = rows.pop()
+            qb = x["q"][0:1, r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+            wb = x["w"][0:1, r:r + 1].cpu().numpy()
+            t1 = time.perf_counter()
+            oi, _ = oracle.two_stage_topk(qb, kcb, wb, spec.m, spec.k, k_blocks=ts["k_blocks"],
+                                          block=ts["block"], q_pos0=r)
+            done += time.perf_counter() - t1
+            pairs += visible_pairs(1, spec.T, spec.m, q_pos0=r)
+            o = set(oi[0, 0].tolist()) - {-1}
+            hits.append(len(set(got[r].tolist()) & o) / max(1, len(o)))
+        rec["cpu_baseline"] = {
+            "value": pairs / done if done > 0 else 0.0, "unit": "pairs/s",
+            "cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model_name(),
+            "kind": "oracle",
+            "sample": f"{len(hits)} query rows that see > 2048 complete blocks, the float64 "
+                      f"two-stage oracle, {pairs} visible pairs in {done:.1f} s"}
+        rec["oracle_sample_recall"] = {"rows": len(hits), "mean": float(np.mean(hits)),
+                                       "min": float(np.min(hits))}
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def cpu_model_name():
@@ -250,6 +367,8 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     spec = synth.CONFIGS[WORKLOAD_SPEC.get(args.workload, args.workload)]
+    if args.workload in TWO_STAGE:
+        return bench_two_stage(args, spec, dev)
     fp8_q = args.workload in FP8_Q
     capacity = None
     if args.workload == "million" and args.mode == "bench":

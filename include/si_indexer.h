@@ -222,15 +222,75 @@ si_status si_indexer_merge_chunk(int64_t B, int64_t S, int64_t T, int32_t H, int
  * SI_FP8_E4M3FN) and w of si_indexer_topk: since the scale is positive,
  * w * ReLU(scale * z) = w_eff * ReLU(z).
  *
- *  q       [rows, H, D] bf16 (rows = B * S), 8-byte aligned
+ *  q       [rows, H, D] bf16 (rows = B * S), 16-byte aligned
  *  w       [rows, H]    fp32
- *  q8      [rows, H, D] E4M3 bytes out, 4-byte aligned
+ *  q8      [rows, H, D] E4M3 bytes out, 8-byte aligned
  *  w_eff   [rows, H]    fp32 out
  *  q_scale [rows, H]    fp32 out, or NULL
  * D = 128, 1 <= H <= 128.  rows = 0 is a no-op.  Asynchronous on stream.
  */
 si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_t H, int32_t D,
                              void* q8, float* w_eff, float* q_scale, void* stream);
+
+/*
+ * ---- Two-stage (coarse -> fine) indexer --------------------------------------------
+ * The candidate stage of the chengshu blog page "两级稀疏注意力：滑窗、压缩 KV latent 与
+ * indexer", section "indexer：在摘要里做'预筛选'": blocks of `block` compressed keys are
+ * scored cheaply and the best k_blocks blocks kept (the page: 2048 blocks of 8), then
+ * only the kept keys are scored and the top k (512 there) returned.  The page defines
+ * no block score; readings used here:
+ *   - block key j = bf16(fp32 sum of keys block*j .. block*j + block-1 in key order,
+ *     times 1/block), rounded to nearest even (si_block_keys_mean);
+ *   - block j is a candidate for query position t once all its keys are visible:
+ *     (block*j + block) * m <= t + 1; the coarse stage is the single-stage indexer
+ *     over the block keys with mask ratio block * m, k = k_blocks;
+ *   - the fine candidates are the keys of the kept blocks plus the visible keys of the
+ *     query's trailing incomplete block; the fine score is the single-stage score,
+ *     computed by the same MFMA sequence and head order, so equal bit for bit.
+ * When a query sees at most k_blocks complete blocks every visible key is a fine
+ * candidate and the row equals si_indexer_topk's.
+ */
+typedef struct si_two_stage_plan {
+    int32_t query_chunk;      /* query rows per driver step                         */
+    int32_t n_chunks;         /* driver steps per batch entry                       */
+    int32_t cand_stride;      /* candidate slots per query row in the workspace     */
+    int32_t reserved;
+    int64_t workspace_bytes;  /* bytes si_indexer_topk_two_stage needs              */
+} si_two_stage_plan;
+
+/*
+ * si_block_keys_mean -- block keys kb [B, T / block, D] bf16 from bf16 keys kc [B, T, D]
+ * (the reading above; keys past the last complete block have no block key).  block a
+ * power of two in 2 .. 64, D = 128, 16-byte aligned pointers.  Asynchronous on stream.
+ */
+si_status si_block_keys_mean(const void* kc, si_dtype kc_dtype, int64_t B, int64_t T, int32_t D,
+                             int32_t block, void* kb, void* stream);
+
+/*
+ * si_indexer_two_stage_plan -- validate a two-stage problem and return its plan (host
+ * only).  cfg: query_chunk = query rows per driver step (0 = auto, 4096); key_tile and
+ * key_partition are passed to the coarse stage.  H <= 64, block a power of two in
+ * 2 .. 64, 1 <= k, k_blocks <= 2048.
+ */
+si_status si_indexer_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
+                                    int32_t m, int32_t k, int32_t k_blocks, int32_t block,
+                                    int64_t q_pos0, const si_config* cfg,
+                                    si_two_stage_plan* out);
+
+/*
+ * si_indexer_topk_two_stage -- two-stage top-k.  q [B, S, H, D] bf16, kc [B, T, D] bf16,
+ * kb [B, T / block, D] bf16 block keys of kc (si_block_keys_mean), w [B, S, H] fp32.
+ * out_idx / out_score [B, S, k]: the same contract as si_indexer_topk (sorted by score
+ * desc, index asc; -1 / -inf padding).  workspace: at least plan.workspace_bytes,
+ * 256-byte aligned (coarse workspace, the kept block lists and the fine candidate keys
+ * of one query chunk).  Per chunk: the coarse indexer, fine scoring, fine selection.
+ */
+si_status si_indexer_topk_two_stage(const void* q, si_dtype q_dtype, const void* kc,
+                                    si_dtype kc_dtype, const void* kb, const float* w, int64_t B,
+                                    int64_t S, int64_t T, int32_t H, int32_t D, int32_t m,
+                                    int32_t k, int32_t k_blocks, int32_t block, int64_t q_pos0,
+                                    const si_config* cfg, int32_t* out_idx, float* out_score,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * si_materialize_scores -- reference path, score write-out.  Writes the head-summed

@@ -8,6 +8,10 @@ it loads the library and fails if it has not been built.
 from . import _lib
 from .api import (  # noqa: F401
     Plan,
+    TwoStagePlan,
+    block_keys,
+    indexer_topk_two_stage,
+    two_stage_plan,
     indexer_merge_chunk,
     indexer_select_chunk,
     indexer_topk,
@@ -23,6 +27,6 @@ from ._lib import SiError  # noqa: F401
 _lib.load()
 
 __all__ = [
-    "Plan", "SiError", "indexer_topk", "indexer_select_chunk", "indexer_merge_chunk",
+    "Plan", "TwoStagePlan", "block_keys", "indexer_topk_two_stage", "two_stage_plan", "SiError", "indexer_topk", "indexer_select_chunk", "indexer_merge_chunk",
     "materialize_scores", "materialize_topk", "plan", "quantize_q", "workspace", "workspace_bytes",
 ]

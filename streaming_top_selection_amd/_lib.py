@@ -27,6 +27,12 @@ class SiPlan(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64)]
 
 
+class SiTwoStagePlan(ctypes.Structure):
+    _fields_ = [("query_chunk", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+                ("cand_stride", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -50,6 +56,12 @@ SIGNATURES = {
     "si_indexer_merge_chunk": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _cfgp,
                                       _i32, _p, _p, _p, _sz, _p]),
     "si_quantize_q_e4m3": (_i32, [_p, _p, _i64, _i32, _i32, _p, _p, _p, _p]),
+    "si_block_keys_mean": (_i32, [_p, _i32, _i64, _i64, _i32, _i32, _p, _p]),
+    "si_indexer_two_stage_plan": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i64, _cfgp, ctypes.POINTER(SiTwoStagePlan)]),
+    "si_indexer_topk_two_stage": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _i64, _cfgp, _p, _p, _p,
+                                         _sz, _p]),
     "si_materialize_scores": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32,
                                      _i32, _i64, _i64, _i64, _p, _p]),
     "si_materialize_topk": (_i32, [_p, _i32, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,

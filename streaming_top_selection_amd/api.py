@@ -219,3 +219,63 @@ def quantize_q(q, w, *, out=None, with_scale=False):
     _lib.check(lib.si_quantize_q_e4m3(_ptr(q), _ptr(w), B * S, H, D, _ptr(out[0]), _ptr(out[1]),
                                       _ptr(scale), _stream(q.device)))
     return (*out, scale) if with_scale else out
+
+
+# ---- two-stage (coarse -> fine) indexer ----------------------------------------------
+
+def block_keys(kc, block: int = 8, out=None):
+    """si_block_keys_mean: bf16 block keys [B, T // block, D] (bf16-rounded mean of each
+    block of `block` consecutive keys, fp32 sum in key order)."""
+    if kc.dim() != 3 or kc.dtype != torch.bfloat16 or not kc.is_cuda or not kc.is_contiguous():
+        raise ValueError("kc must be a contiguous bf16 GPU tensor [B, T, D]")
+    B, T, D = kc.shape
+    if out is None:
+        out = torch.empty((B, T // block, D), dtype=torch.bfloat16, device=kc.device)
+    lib = _lib.load()
+    _lib.check(lib.si_block_keys_mean(_ptr(kc), _lib.SI_BF16, B, T, D, block, _ptr(out),
+                                      _stream(kc.device)))
+    return out
+
+
+@dataclass(frozen=True)
+class TwoStagePlan:
+    query_chunk: int
+    n_chunks: int
+    cand_stride: int
+    workspace_bytes: int
+
+
+def two_stage_plan(B, S, T, H=64, D=128, m=4, k=512, k_blocks=2048, block=8, q_pos0=0,
+                   query_chunk=0, key_tile=0, key_partition=0) -> TwoStagePlan:
+    lib = _lib.load()
+    out = _lib.SiTwoStagePlan()
+    cfg = _cfg(key_tile, query_chunk, key_partition)
+    _lib.check(lib.si_indexer_two_stage_plan(B, S, T, H, D, m, k, k_blocks, block, q_pos0,
+                                             ctypes.byref(cfg), ctypes.byref(out)))
+    return TwoStagePlan(out.query_chunk, out.n_chunks, out.cand_stride, out.workspace_bytes)
+
+
+def indexer_topk_two_stage(q, kc, kb, w, m: int, k: int, *, k_blocks: int = 2048,
+                           block: int = 8, q_pos0: int = 0, query_chunk: int = 0,
+                           key_tile: int = 0, key_partition: int = 0, out=None, ws=None):
+    """Two-stage top-k (coarse blocks, then fine keys).  kb = block_keys(kc, block).
+    Returns (idx int32 [B,S,k], score float32 [B,S,k]) like indexer_topk."""
+    B, S, T, H, D, qd, kcd = _shapes(q, kc, w, None)
+    if qd != _lib.SI_BF16 or kcd != _lib.SI_BF16:
+        raise TypeError("the two-stage indexer takes bf16 q and bf16 keys")
+    if tuple(kb.shape) != (B, T // block, D) or kb.dtype != torch.bfloat16 or not kb.is_contiguous():
+        raise ValueError("kb must be the bf16 block keys [B, T // block, D]")
+    pl = two_stage_plan(B, S, T, H, D, m, k, k_blocks, block, q_pos0, query_chunk, key_tile,
+                        key_partition)
+    if out is None:
+        out = (torch.empty((B, S, k), dtype=torch.int32, device=q.device),
+               torch.empty((B, S, k), dtype=torch.float32, device=q.device))
+    if ws is None:
+        ws = torch.empty(max(pl.workspace_bytes, 1), dtype=torch.uint8, device=q.device)
+    cfg = _cfg(key_tile, query_chunk, key_partition)
+    lib = _lib.load()
+    _lib.check(lib.si_indexer_topk_two_stage(
+        _ptr(q), qd, _ptr(kc), kcd, _ptr(kb), _ptr(w), B, S, T, H, D, m, k, k_blocks, block,
+        q_pos0, ctypes.byref(cfg), _ptr(out[0]), _ptr(out[1]), _ptr(ws), ws.numel(),
+        _stream(q.device)))
+    return out

@@ -154,6 +154,71 @@ si_status run_merge(const si::PlanInternal& pl, int64_t B, int64_t S, int64_t T,
     return SI_OK;
 }
 
+// Every query chunk of a planned problem: select then merge, on one stream.
+si_status run_indexer(const si::PlanInternal& pl, const si::Problem& P, int32_t k, int op,
+                      int32_t* out_idx, float* out_score, void* ws, hipStream_t s) {
+    si_status st;
+    for (int32_t c = 0; c < pl.pub.n_chunks; ++c) {
+        if ((st = run_select(pl, P, k, c, ws, op, s)) != SI_OK) return st;
+        if ((st = run_merge(pl, P.B, P.S, P.T, P.m, k, P.q_pos0, c, out_idx, out_score, ws, s)) !=
+            SI_OK)
+            return st;
+    }
+    return SI_OK;
+}
+
+// ---- two-stage plan ---------------------------------------------------------------
+struct TwoStagePlan {
+    int64_t qc, n_chunks, cand_stride;
+    int64_t coarse_ws, cidx_off, cscore_off, cand_off, total;
+};
+
+constexpr int64_t kTwoStageAutoChunk = 4096;
+
+si_config coarse_config(const si_config* cfg) {
+    si_config c = cfg ? *cfg : si_config{0, 0, 0, 0};
+    c.query_chunk = 0;          // the coarse problem of one two-stage chunk is one chunk
+    return c;
+}
+
+si_status make_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D, int32_t m,
+                              int32_t k, int32_t k_blocks, int32_t blk, int64_t q_pos0,
+                              const si_config* cfg, TwoStagePlan& tp) {
+    std::string msg;
+    si_status st = si::check_shape(B, S, T, H, D, m, q_pos0, SI_BF16, msg);
+    if (st != SI_OK) return fail(st, msg);
+    if (k < 1 || k_blocks < 1) return fail(SI_ERR_INVALID_ARG, "k and k_blocks must be >= 1");
+    if (k > si::kPlanMaxK || k_blocks > si::kPlanMaxK)
+        return fail(SI_ERR_UNSUPPORTED, "k and k_blocks must be <= 2048");
+    if (H > 64) return fail(SI_ERR_UNSUPPORTED, "the two-stage indexer is built for H <= 64");
+    if (blk < 2 || blk > 64 || (blk & (blk - 1)) != 0)
+        return fail(SI_ERR_UNSUPPORTED, "block must be a power of two in 2 .. 64");
+    if (cfg && (cfg->reserved != 0 || cfg->query_chunk < 0))
+        return fail(SI_ERR_INVALID_ARG, "invalid si_config");
+    const int64_t qc = (cfg && cfg->query_chunk) ? cfg->query_chunk
+                                                 : std::min<int64_t>(std::max<int64_t>(S, 1),
+                                                                     kTwoStageAutoChunk);
+    tp.qc = qc;
+    tp.n_chunks = (S == 0 || B == 0) ? 0 : si::ceil_div(S, qc);
+    tp.cand_stride = si::round_up((int64_t)blk * k_blocks + blk, 64);
+    // the coarse workspace of the widest chunk plan
+    const si_config cc = coarse_config(cfg);
+    tp.coarse_ws = 0;
+    for (int64_t c = 0; c < tp.n_chunks; ++c) {
+        const int64_t r0 = c * qc, rows = std::min(qc, S - r0);
+        si::PlanInternal pl;
+        st = si::make_plan(1, rows, T / blk, H, D, blk * m, k_blocks, q_pos0 + r0, SI_BF16, &cc,
+                           pl, msg);
+        if (st != SI_OK) return fail(st, "coarse stage: " + msg);
+        tp.coarse_ws = std::max<int64_t>(tp.coarse_ws, pl.pub.workspace_bytes);
+    }
+    tp.cidx_off = si::round_up(tp.coarse_ws, 256);
+    tp.cscore_off = tp.cidx_off + si::round_up(qc * k_blocks * 4, 256);
+    tp.cand_off = tp.cscore_off + si::round_up(qc * k_blocks * 4, 256);
+    tp.total = tp.n_chunks == 0 ? 0 : tp.cand_off + qc * tp.cand_stride * 8;
+    return SI_OK;
+}
+
 // The device address of `scratch` on the current device, looked up on the first call
 // on each device and kept.
 si_status scratch_on_current_device(void** out) {
@@ -328,9 +393,10 @@ si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_
     if (H > si::kPlanMaxH) return fail(SI_ERR_UNSUPPORTED, "H must be <= 128");
     if (rows == 0) return SI_OK;
     if (!q || !w || !q8 || !w_eff) return fail(SI_ERR_INVALID_ARG, "q, w, q8 and w_eff must not be NULL");
-    if (!aligned(q, 8) || !aligned(q8, 4) || !aligned(w, 4) || !aligned(w_eff, 4) ||
+    if (!aligned(q, 16) || !aligned(q8, 8) || !aligned(w, 4) || !aligned(w_eff, 4) ||
         (q_scale && !aligned(q_scale, 4)))
-        return fail(SI_ERR_INVALID_ARG, "q must be 8-byte aligned, q8, w, w_eff and q_scale 4-byte");
+        return fail(SI_ERR_INVALID_ARG,
+                    "q must be 16-byte aligned, q8 8-byte, w, w_eff and q_scale 4-byte");
     si::QuantArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.w = w;
@@ -340,6 +406,118 @@ si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_
     a.nvec = rows * H;
     const hipError_t e = si::launch_quantize_q(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "quantize kernel launch");
+    return SI_OK;
+}
+
+si_status si_block_keys_mean(const void* kc, si_dtype kc_dtype, int64_t B, int64_t T, int32_t D,
+                             int32_t block, void* kb, void* stream) {
+    g_last_error.clear();
+    if (B < 0 || T < 0) return fail(SI_ERR_INVALID_ARG, "B and T must be >= 0");
+    if (kc_dtype != SI_BF16) return fail(SI_ERR_UNSUPPORTED, "block keys are built from bf16 keys");
+    if (D != si::kPlanD) return fail(SI_ERR_UNSUPPORTED, "only D = 128 is built");
+    if (block < 2 || block > 64 || (block & (block - 1)) != 0)
+        return fail(SI_ERR_UNSUPPORTED, "block must be a power of two in 2 .. 64");
+    if (B == 0 || T / block == 0) return SI_OK;
+    if (!kc || !kb) return fail(SI_ERR_INVALID_ARG, "kc and kb must not be NULL");
+    if (!aligned(kc, 16) || !aligned(kb, 16))
+        return fail(SI_ERR_INVALID_ARG, "kc and kb must be 16-byte aligned");
+    si::BlockKeyArgs a;
+    a.kc = static_cast<const uint16_t*>(kc);
+    a.kb = static_cast<uint16_t*>(kb);
+    a.B = B;
+    a.T = T;
+    a.blk = block;
+    const hipError_t e = si::launch_block_keys(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block key kernel launch");
+    return SI_OK;
+}
+
+si_status si_indexer_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
+                                    int32_t m, int32_t k, int32_t k_blocks, int32_t block,
+                                    int64_t q_pos0, const si_config* cfg,
+                                    si_two_stage_plan* out) {
+    g_last_error.clear();
+    if (!out) return fail(SI_ERR_INVALID_ARG, "out must not be NULL");
+    TwoStagePlan tp;
+    const si_status st = make_two_stage_plan(B, S, T, H, D, m, k, k_blocks, block, q_pos0, cfg, tp);
+    if (st != SI_OK) return st;
+    out->query_chunk = (int32_t)tp.qc;
+    out->n_chunks = (int32_t)tp.n_chunks;
+    out->cand_stride = (int32_t)tp.cand_stride;
+    out->reserved = 0;
+    out->workspace_bytes = tp.total;
+    return SI_OK;
+}
+
+si_status si_indexer_topk_two_stage(const void* q, si_dtype q_dtype, const void* kc,
+                                    si_dtype kc_dtype, const void* kb, const float* w, int64_t B,
+                                    int64_t S, int64_t T, int32_t H, int32_t D, int32_t m,
+                                    int32_t k, int32_t k_blocks, int32_t block, int64_t q_pos0,
+                                    const si_config* cfg, int32_t* out_idx, float* out_score,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (q_dtype != SI_BF16 || kc_dtype != SI_BF16)
+        return fail(SI_ERR_UNSUPPORTED, "the two-stage indexer takes bf16 q and bf16 keys");
+    TwoStagePlan tp;
+    si_status st = make_two_stage_plan(B, S, T, H, D, m, k, k_blocks, block, q_pos0, cfg, tp);
+    if (st != SI_OK) return st;
+    if ((st = check_inputs(q, q_dtype, kc, kc_dtype, nullptr, w, B, S, T)) != SI_OK) return st;
+    if (B > 0 && T / block > 0 && (!kb || !aligned(kb, 16)))
+        return fail(SI_ERR_INVALID_ARG, "kb must be non-NULL and 16-byte aligned");
+    if (B > 0 && S > 0 && (!out_idx || !out_score))
+        return fail(SI_ERR_INVALID_ARG, "outputs must not be NULL");
+    if ((int64_t)workspace_bytes < tp.total)
+        return fail(SI_ERR_WORKSPACE, "workspace smaller than si_two_stage_plan.workspace_bytes");
+    if (tp.total > 0 && (!workspace || !aligned(workspace, 256)))
+        return fail(SI_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* cidx = reinterpret_cast<int32_t*>(ws + tp.cidx_off);
+    float* cscore = reinterpret_cast<float*>(ws + tp.cscore_off);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws + tp.cand_off);
+    const int64_t nb = T / block;
+    const si_config cc = coarse_config(cfg);
+    std::string msg;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint16_t* qb = static_cast<const uint16_t*>(q) + b * S * H * (int64_t)D;
+        const float* wb = w + b * S * H;
+        const uint16_t* kcb = static_cast<const uint16_t*>(kc) + b * T * (int64_t)D;
+        const uint16_t* kbb = static_cast<const uint16_t*>(kb) + b * nb * (int64_t)D;
+        for (int64_t c = 0; c < tp.n_chunks; ++c) {
+            const int64_t r0 = c * tp.qc, rows = std::min(tp.qc, S - r0);
+            // coarse: the single-stage indexer over the block keys, mask ratio block * m
+            si::PlanInternal pl;
+            st = si::make_plan(1, rows, nb, H, D, block * m, k_blocks, q_pos0 + r0, SI_BF16, &cc,
+                               pl, msg);
+            if (st != SI_OK) return fail(st, "coarse stage: " + msg);
+            const si::Problem P = make_problem(qb + r0 * H * (int64_t)D, kbb, nullptr, wb + r0 * H,
+                                               1, rows, nb, H, block * m, q_pos0 + r0);
+            if ((st = run_indexer(pl, P, k_blocks, si::kOpBf16, cidx, cscore, ws, s)) != SI_OK)
+                return st;
+            // fine: score the candidates, select the top-k into the output rows
+            si::FineArgs a;
+            a.q = qb + r0 * H * (int64_t)D;
+            a.w = wb + r0 * H;
+            a.kc = kcb;
+            a.cidx = cidx;
+            a.cand = cand;
+            a.out_idx = out_idx + (b * S + r0) * (int64_t)k;
+            a.out_score = out_score + (b * S + r0) * (int64_t)k;
+            a.T = T;
+            a.rows = rows;
+            a.q_pos0 = q_pos0 + r0;
+            a.cand_stride = tp.cand_stride;
+            a.H = H;
+            a.m = m;
+            a.blk = block;
+            a.k_blocks = k_blocks;
+            a.k = k;
+            hipError_t e = si::launch_fine_score(a, s);
+            if (e != hipSuccess) return hip_fail(e, "fine score kernel launch");
+            e = si::launch_fine_select(a, s);
+            if (e != hipSuccess) return hip_fail(e, "fine select kernel launch");
+        }
+    }
     return SI_OK;
 }
 

@@ -70,6 +70,33 @@ struct QuantArgs {
 
 hipError_t launch_quantize_q(const QuantArgs& a, hipStream_t stream);
 
+// Two-stage indexer: block keys (mean of blk consecutive bf16 keys).
+struct BlockKeyArgs {
+    const uint16_t* kc;    // [B, T, kD] bf16
+    uint16_t* kb;          // [B, T / blk, kD] bf16
+    int64_t B, T;
+    int32_t blk;
+};
+
+// Two-stage indexer: fine scoring and selection of one query chunk of one batch entry.
+struct FineArgs {
+    const uint16_t* q;     // [rows, H, kD] bf16: the chunk's query rows
+    const float* w;        // [rows, H]
+    const uint16_t* kc;    // [T, kD] bf16 keys of the batch entry
+    const int32_t* cidx;   // [rows, k_blocks] kept block indices (coarse top-k)
+    uint64_t* cand;        // [rows, cand_stride] candidate selection keys
+    int32_t* out_idx;      // [rows, k] output rows
+    float* out_score;      // [rows, k]
+    int64_t T, rows;
+    int64_t q_pos0;        // absolute position of the chunk's first row
+    int64_t cand_stride;
+    int32_t H, m, blk, k_blocks, k;
+};
+
+hipError_t launch_block_keys(const BlockKeyArgs& a, hipStream_t stream);
+hipError_t launch_fine_score(const FineArgs& a, hipStream_t stream);
+hipError_t launch_fine_select(const FineArgs& a, hipStream_t stream);
+
 // op: operand mode (kOpBf16 .. kOpF8K4, si_score.hpp)
 hipError_t launch_select(const SelectArgs& a, int nwave, int kb, int nsub, int cg, int op,
                          hipStream_t stream);

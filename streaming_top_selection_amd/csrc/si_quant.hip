@@ -15,42 +15,67 @@
 namespace si {
 
 constexpr int kQuantWaves = 4;
+constexpr int kQuantUnroll = 2;        // vector groups per wave and iteration (loads in flight)
 
-// One wave per two vectors of D = 128: half hh of the wave holds vector 2*g + hh, each
-// lane four consecutive elements.
+// One vector of D = 128 per 16 lanes (8 elements, 16 bytes, per lane), four vectors per
+// wave and group; waves stride over the groups, kQuantUnroll groups at a time.
 __global__ void __launch_bounds__(kQuantWaves * 64) quantize_q_kernel(QuantArgs A) {
     const int lane = lane_id();
-    const int il = lane & 31;
-    const int64_t g = (int64_t)blockIdx.x * kQuantWaves + wave_id();
-    const int64_t vec = 2 * g + (lane >> 5);
-    const bool live = vec < A.nvec;
-    u32x2 raw = {0u, 0u};
-    if (live) raw = *reinterpret_cast<const u32x2*>(A.q + vec * kD + 4 * il);
-    const float f[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
-                        __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
-    float amax = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
-    // maximum over the 32 lanes of this half (xor distances below 32 stay in the half)
+    const int sub = lane & 15;
+    const int64_t ngroups = (A.nvec + 3) / 4;
+    const int64_t wave_g = (int64_t)blockIdx.x * kQuantWaves + wave_id();
+    const int64_t nwaves = (int64_t)gridDim.x * kQuantWaves;
+    for (int64_t g0 = wave_g * kQuantUnroll; g0 < ngroups; g0 += nwaves * kQuantUnroll) {
+        u32x4 raw[kQuantUnroll];
+        int64_t vec[kQuantUnroll];
 #pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-    float x[4];
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            vec[u] = 4 * (g0 + u) + (lane >> 4);
+            raw[u] = u32x4{0u, 0u, 0u, 0u};
+            if (vec[u] < A.nvec)
+                raw[u] = *reinterpret_cast<const u32x4*>(A.q + vec[u] * kD + 8 * sub);
+        }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(f[i] / scale, -448.0f), 448.0f);
-    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-    packed = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], packed, true);
-    if (live) {
-        *reinterpret_cast<int*>(A.q8 + vec * kD + 4 * il) = packed;
-        if (il == 0) {
-            A.w_eff[vec] = A.w[vec] * scale;
-            if (A.q_scale) A.q_scale[vec] = scale;
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            float f[8];
+            const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(wd[i] << 16);
+                f[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            // maximum over the 16 lanes of this vector (xor distances below 16)
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+            const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = fminf(fmaxf(f[i] / scale, -448.0f), 448.0f);
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+            if (vec[u] < A.nvec) {
+                *reinterpret_cast<u32x2*>(A.q8 + vec[u] * kD + 8 * sub) =
+                    u32x2{(uint32_t)lo, (uint32_t)hi};
+                if (sub == 0) {
+                    A.w_eff[vec[u]] = A.w[vec[u]] * scale;
+                    if (A.q_scale) A.q_scale[vec[u]] = scale;
+                }
+            }
         }
     }
 }
 
 hipError_t launch_quantize_q(const QuantArgs& a, hipStream_t stream) {
     if (a.nvec <= 0) return hipSuccess;
-    const int64_t waves = (a.nvec + 1) / 2;
-    const int64_t grid = (waves + kQuantWaves - 1) / kQuantWaves;
+    // enough waves to fill every SIMD; each strides over the remaining groups
+    const int64_t groups = (a.nvec + 3) / 4;
+    const int64_t want = (groups + kQuantUnroll * kQuantWaves - 1) / (kQuantUnroll * kQuantWaves);
+    const int64_t grid = want < 2048 ? want : 2048;
     hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)grid), dim3(kQuantWaves * 64), 0,
                        stream, a);
     return hipGetLastError();

@@ -1,0 +1,242 @@
+// Two-stage (coarse -> fine) indexer kernels: the candidate stage of the chengshu blog
+// page "两级稀疏注意力：滑窗、压缩 KV latent 与 indexer" (section "indexer：在摘要里做
+// '预筛选'"): blocks of compressed keys are scored cheaply, the best blocks are kept,
+// and only their keys are scored finely.  Readings (the page defines no block score):
+// a block key is the bf16-rounded mean of the block's keys; a block is a candidate once
+// all of its keys are visible; the fine candidates are the kept blocks' keys plus the
+// query's trailing incomplete block.
+//
+// The coarse stage is the single-stage indexer over the block keys (mask ratio
+// block * m), run by the driver.  The kernels here build the block keys, score the fine
+// candidates and select the final top-k.
+//
+// Fine scoring keeps the single-stage arithmetic bit for bit: one wave holds one query's
+// heads as MFMA rows (A) and 32 gathered keys as columns (B), with the same
+// v_mfma_f32_32x32x16_bf16 chain over the same d positions per step as score_regs_bf16,
+// then the same head-ordered epilogue acc = fmaf(w_h, max(z_h, 0), acc).
+#include "si_kernels.hpp"
+#include "si_sort.hpp"
+
+namespace si {
+
+// ---------------------------------------------------------------------------
+// Block keys: kb[b, j, :] = bf16(fp32(k[b, blk j] + ... + k[b, blk j + blk - 1]) / blk),
+// the sum taken in key order, 1/blk a power of two (exact), rounded to nearest even.
+// One thread per (block, 8 consecutive d): 16-byte loads and stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // finite x
+}
+
+__global__ void __launch_bounds__(256) block_keys_kernel(BlockKeyArgs A) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nb = A.T / A.blk;
+    constexpr int kChunks = kD / 8;
+    if (id >= A.B * nb * kChunks) return;
+    const int dch = (int)(id % kChunks);
+    const int64_t bj = id / kChunks;                 // b * nb + j
+    const int64_t b = bj / nb, j = bj - b * nb;
+    const uint16_t* src = A.kc + ((b * A.T + j * A.blk) * kD + 8 * dch);
+    float acc[8];
+    {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = __uint_as_float(wd[i] << 16);
+            acc[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+        }
+    }
+    for (int i = 1; i < A.blk; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)i * kD);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = acc[2 * e] + __uint_as_float(wd[e] << 16);
+            acc[2 * e + 1] = acc[2 * e + 1] + __uint_as_float(wd[e] & 0xFFFF0000u);
+        }
+    }
+    const float inv = 1.0f / (float)A.blk;           // exact: blk is a power of two
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = f32_to_bf16_rne(acc[2 * e] * inv) | (f32_to_bf16_rne(acc[2 * e + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(A.kb + (bj * kD + 8 * dch)) = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+hipError_t launch_block_keys(const BlockKeyArgs& a, hipStream_t stream) {
+    const int64_t n = a.B * (a.T / a.blk) * (kD / 8);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(block_keys_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fine scoring: one wave per query row, 64 candidate positions per iteration.
+// Candidate position p of row r: p < blk*nk -> key blk * cidx[r][p / blk] + p % blk (the
+// kept blocks, nk = min(k_blocks, complete visible blocks)); then the trailing keys
+// blk*nb .. n-1; past ncand nothing.  Writes the selection key (ord(score), ~index) of
+// each candidate to cand[r][p].
+// ---------------------------------------------------------------------------
+constexpr int kFineWaves = 4;
+
+struct FineRow {
+    int64_t n, nb, nk, ncand;
+};
+
+__device__ __forceinline__ FineRow fine_row(const FineArgs& A, int64_t t) {
+    FineRow f;
+    f.n = visible_keys(t, A.m, A.T);
+    f.nb = visible_keys(t, A.blk * A.m, A.T / A.blk);
+    f.nk = min(f.nb, (int64_t)A.k_blocks);
+    f.ncand = A.blk * f.nk + (f.n - A.blk * f.nb);
+    return f;
+}
+
+__device__ __forceinline__ int64_t fine_key(const FineArgs& A, const int32_t* cidx,
+                                            const FineRow& f, int64_t p) {
+    if (p < A.blk * f.nk) return (int64_t)cidx[p / A.blk] * A.blk + p % A.blk;
+    if (p < f.ncand) return A.blk * f.nb + (p - A.blk * f.nk);
+    return -1;
+}
+
+__global__ void __launch_bounds__(kFineWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fine_score_kernel(FineArgs A) {
+    const int lane = lane_id();
+    const int hh = lane >> 5, il = lane & 31;
+    const int64_t r = (int64_t)blockIdx.x * kFineWaves + wave_id();
+    if (r >= A.rows) return;                          // wave-uniform
+    const int64_t t = A.q_pos0 + r;                    // absolute position of this row
+    const FineRow f = fine_row(A, t);
+    const int32_t* cidx = A.cidx + r * A.k_blocks;
+    uint64_t* out = A.cand + r * A.cand_stride;
+    const int H = A.H;
+
+    // A operand: heads 32 rb + il of this query, d = 64 hh + 8 s + [0, 8) in step s
+    bf16x8 qa[2][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int head = 32 * rb + il;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (head < H)
+                v = *reinterpret_cast<const u32x4*>(A.q + ((r * H + head) * kD + 64 * hh + 8 * s));
+            qa[rb][s] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    const float* wrow = A.w + r * H;
+
+    const int64_t nchunks = (f.ncand + 63) / 64;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        // B operand: key block kb holds positions 64 c + 32 kb + [0, 32); lane il of each
+        // half supplies its column, d = 64 hh + 8 s + [0, 8)
+        bf16x8 kf[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int64_t key = fine_key(A, cidx, f, 64 * c + 32 * kb + il);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (key >= 0)
+                    v = *reinterpret_cast<const u32x4*>(A.kc + (key * kD + 64 * hh + 8 * s));
+                kf[kb][s] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        f32x16 z[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) z[rb][kb][e] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) z[rb][kb] = mfma32x32x16(qa[rb][s], kf[kb][s], z[rb][kb]);
+            }
+        // Lane il of half hh scores position 64 c + 32 hh + il, i.e. column il of key
+        // block hh.  Register e of lane (il, half g) holds head 32 rb + mfma_row(e, 32 g)
+        // of that column, so a lane keeps its own half's heads of block hh and receives
+        // the other half's from lane ^ 32.
+        float own[2][16], oth[2][16];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                own[rb][e] = hh ? z[rb][1][e] : z[rb][0][e];
+                const float send = hh ? z[rb][0][e] : z[rb][1][e];
+                oth[rb][e] = __shfl_xor(send, 32);
+            }
+        // acc = fmaf(w_h, max(z_h, 0), acc) for h = 0 .. H-1 from +0, as in the tile
+        float acc = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 64; ++h) {
+            if (h < H) {
+                const int rb = h >> 5, hl = h & 31;
+                const int e = 4 * (hl >> 3) + (hl & 3);
+                const float zz = (((hl >> 2) & 1) == hh) ? own[rb][e] : oth[rb][e];
+                acc = __builtin_fmaf(wrow[h], __builtin_fmaxf(zz, 0.0f), acc);
+            }
+        }
+        const int64_t p = 64 * c + lane;
+        const int64_t key = fine_key(A, cidx, f, p);
+        out[p] = key >= 0 ? make_key(canon_zero(acc), (uint32_t)key) : 0ull;
+    }
+}
+
+hipError_t launch_fine_score(const FineArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    const int64_t grid = (a.rows + kFineWaves - 1) / kFineWaves;
+    hipLaunchKernelGGL(fine_score_kernel, dim3((unsigned)grid), dim3(kFineWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fine selection: one wave per row.  The k-th largest candidate key by an exact radix
+// select over the row's keys (read from the workspace), the keys at or above it
+// gathered into LDS, sorted in registers by the bitonic network, written as the row.
+// ---------------------------------------------------------------------------
+template <int LE>
+__global__ void __launch_bounds__(64) fine_select_kernel(FineArgs A) {
+    constexpr int EPL = 1 << LE;
+    __shared__ uint64_t sbuf[64 * EPL];
+    __shared__ uint32_t hist[256];
+    const int lane = lane_id();
+    const int64_t r = blockIdx.x;
+    const int64_t t = A.q_pos0 + r;
+    const FineRow f = fine_row(A, t);
+    const uint64_t* keys = A.cand + r * A.cand_stride;
+    const int ncand = (int)f.ncand;
+    const int need = min(ncand, A.k);
+    // exactly `need` keys are >= th (keys are unique and non-zero)
+    uint64_t th = 1ull;
+    if (ncand > A.k) th = wave_select_kth(LdsKeys{keys, ncand}, A.k, hist);
+    int pos = 0;
+    for (int base = 0; base < ncand; base += 64) {
+        const int i = base + lane;
+        const uint64_t v = i < ncand ? keys[i] : 0ull;
+        const bool keep = i < ncand && v >= th;
+        const uint64_t bal = __ballot(keep);
+        if (keep) sbuf[pos + __popcll(bal & lanemask_lt())] = v;
+        pos += __popcll(bal);
+    }
+    wave_sync();
+    uint64_t x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < need ? sbuf[EPL * lane + e] : 0ull;
+    sort_desc<LE>(x);
+    write_sorted_keys<LE>(A.out_idx + r * (int64_t)A.k, A.out_score + r * (int64_t)A.k, A.k, x,
+                          need, lane);
+}
+
+hipError_t launch_fine_select(const FineArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    const dim3 grid((unsigned)a.rows), block(64);
+    if (a.k <= 512) hipLaunchKernelGGL(fine_select_kernel<3>, grid, block, 0, stream, a);
+    else if (a.k <= 1024) hipLaunchKernelGGL(fine_select_kernel<4>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(fine_select_kernel<5>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace si
