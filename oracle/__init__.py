@@ -22,3 +22,4 @@ from .indexer import (  # noqa: F401
 )
 from .quant import E4M3_MAX, e4m3fn_encode_rne, quantize_q_e4m3  # noqa: F401,E402
 from .two_stage import block_keys_mean, f32_to_bf16_bits_rne, two_stage_topk  # noqa: F401,E402
+from .attention import attention_error_bound, default_scale, sparse_attention  # noqa: F401,E402
