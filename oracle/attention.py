@@ -55,12 +55,15 @@ def attention_error_bound(qa_bits, kv_bits, idx, scale: float, *, rows=None):
     bf16 for the weight x value product (fp32 accumulation), normalised by the fp32
     sum of the unrounded weights, output rounded to bf16.
 
-    With w_j the exact weights and A_d = sum_j w_j |v_jd|: each weight is off by a
-    factor 1 + e_j with |e_j| <= eps_w = 2^-9 (bf16 rounding) + 2 dz (the logit error
-    dz in natural-log units, entering numerator and denominator) + 2^-20 (exp2 and the
-    running-maximum rescales) + (n + 8) 2^-24 (fp32 sums), so the output is off by at
-    most 2 eps_w A_d before its own bf16 rounding (2^-9 |o_d|, o the exact output):
-        beta[d] = 2 eps_w A_d + 2^-9 (|o_d| + 2 eps_w A_d).
+    bf16 keeps 8 significant bits, so rounding to it changes a value by at most 2^-8
+    of itself.  With w_j the exact weights and A_d = sum_j w_j |v_jd|, each computed
+    weight is w_j (1 + e_j) with |e_j| <= eps_w = 2^-8 (its bf16 rounding) + 2 dz (the
+    logit error dz in natural-log units, entering the weight and the maximum) + 2^-20
+    (exp2 and the running-maximum rescales) + (n + 8) 2^-24 (the fp32 sums, the
+    reciprocal and the final product), to first order, so before its own bf16 rounding
+    the output is off by at most eps_w A_d (times 1 + 2^-6 for the second-order terms);
+    that rounding adds 2^-8 of the output's magnitude:
+        beta[d] = c eps_w A_d + 2^-8 (|o_d| + c eps_w A_d),   c = 1 + 2^-6.
     dz = (D + 4) 2^-24 |scale| max_j sum_d |qa_d kv_jd| (dot forward error, the scale
     products and the log2(e) factor)."""
     qa_bits = np.asarray(qa_bits)
@@ -71,6 +74,7 @@ def attention_error_bound(qa_bits, kv_bits, idx, scale: float, *, rows=None):
     o = sparse_attention(qa_bits, kv_bits, idx, scale, rows=rows)
     out = np.zeros_like(o)
     u = 2.0 ** -24
+    c = 1.0 + 2.0 ** -6
     for b in range(B):
         for i, t in enumerate(rows):
             sel = idx[b, t][idx[b, t] >= 0]
@@ -83,10 +87,10 @@ def attention_error_bound(qa_bits, kv_bits, idx, scale: float, *, rows=None):
             p = np.exp(logits - logits.max(axis=1, keepdims=True))
             w = p / p.sum(axis=1, keepdims=True)                # [HA, n]
             dz = (D + 4) * u * abs(scale) * (np.abs(q) @ np.abs(k).T).max(axis=1)   # [HA]
-            eps_w = 2.0 ** -9 + 2 * dz + 2.0 ** -20 + (n + 8) * u
+            eps_w = 2.0 ** -8 + 2 * dz + 2.0 ** -20 + (n + 8) * u
             A = w @ np.abs(k)                                   # [HA, D]
-            e = 2 * eps_w[:, None] * A
-            out[b, i] = e + 2.0 ** -9 * (np.abs(o[b, i]) + e)
+            e = c * eps_w[:, None] * A
+            out[b, i] = e + 2.0 ** -8 * (np.abs(o[b, i]) + e)
     return out
 
 
