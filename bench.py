@@ -55,14 +55,21 @@ WORKLOADS["long-two-stage"] = (
     "block keys = bf16 mean of 8 keys, coarse top-2048 blocks, fine top-512 of their keys "
     "(+ the trailing incomplete block), bf16")
 TWO_STAGE = {"long-two-stage": dict(block=8, k_blocks=2048)}
+WORKLOADS["compose-long"] = (
+    "Indexer composed with the sparse-attention consumer at the long-context shape: B=1, "
+    "S=262144, m=4, T=65536, H_I=64, D=128, top-k=512 (streaming indexer), then softmax "
+    "attention of 64 heads over the 512 selected compressed latents (key = value, D=128), "
+    "bf16")
+COMPOSE = {"compose-long": dict(HA=64)}
 # workload -> input configuration (synth.CONFIGS); the fp8-q workloads quantise q in the step
 WORKLOAD_SPEC = {"v4flash-fp8": "v4flash-e4m3", "v4flash-mxfp4": "v4flash-mxfp4",
-                 "long-two-stage": "long"}
+                 "long-two-stage": "long", "compose-long": "long"}
 FP8_Q = {"v4flash-fp8", "v4flash-mxfp4"}
 DTYPE_NAME = {("bf16", "bf16"): "bf16", ("bf16", "e4m3fn"): "bf16",
               ("e4m3fn", "e4m3fn"): "e4m3", ("e4m3fn", "mxfp4"): "e4m3xe2m1"}
 # default (steps, warmup) per workload: about a minute of timed work at most
-DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1), "long-two-stage": (5, 1)}
+DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1), "long-two-stage": (5, 1),
+                 "compose-long": (5, 1)}
 # q rows per slice of the million workload's streamed-q capacity pass
 CAPACITY_SLICE_ROWS = 16384
 
@@ -213,6 +220,110 @@ def bench_two_stage(args, spec, dev):
                       f"two-stage oracle, {pairs} visible pairs in {done:.1f} s"}
         rec["oracle_sample_recall"] = {"rows": len(hits), "mean": float(np.mean(hits)),
                                        "min": float(np.min(hits))}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_compose(args, spec, dev):
+    """One step = the streaming indexer top-k (si_indexer_topk) then the sparse attention
+    over its selection (si_sparse_attention), inputs resident."""
+    import numpy as np
+    import torch
+
+    import streaming_top_selection_amd as si
+    import synth
+    HA = COMPOSE[args.workload]["HA"]
+    x = synth.make_inputs(spec, device=dev)
+    qa, kv = synth.gen_attention_inputs(spec, HA, device=dev)
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    input_bytes = tensor_bytes(x["q"], x["kc"], x["w"], qa, kv)
+    pl = si.plan(spec.B, spec.S, spec.T, spec.H, spec.D, spec.m, spec.k)
+    ws = si.workspace(pl, dev)
+    sel = (torch.empty((spec.B, spec.S, spec.k), dtype=torch.int32, device=dev),
+           torch.empty((spec.B, spec.S, spec.k), dtype=torch.float32, device=dev))
+    o = torch.empty((spec.B, spec.S, HA, spec.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        si.indexer_topk(x["q"], x["kc"], x["w"], spec.m, spec.k, out=sel, ws=ws)
+        if ev:
+            ev[1].record(stream)
+        si.sparse_attention(qa, kv, sel[0], out=o)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    step_s = wall / args.steps
+    ix_s = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) / 1e3
+    at_s = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs) / 1e3
+    peak = torch.cuda.max_memory_allocated(dev)
+    vis = spec.B * visible_pairs(spec.S, spec.T, spec.m)
+    t = np.arange(spec.S, dtype=np.int64)
+    nsel = int(np.minimum(spec.k, np.minimum(spec.T, (t + 1) // spec.m)).sum()) * spec.B
+    at_flops = nsel * HA * spec.D * 4              # score and value products, 2 flop each
+    ix_flops = vis * 2 * spec.H * spec.D
+    rec = {
+        "metric": METRIC, "value": vis / step_s, "unit": "pairs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "B": spec.B, "S": spec.S, "T": spec.T,
+                   "H_I": spec.H, "D": spec.D, "m": spec.m, "k": spec.k, "H_A": HA},
+        "value_note": "value = the indexer's causally visible pairs per second of the whole "
+                      "composed step (indexer + attention)",
+        "indexer_ms": ix_s * 1e3, "attention_ms": at_s * 1e3,
+        "peak_hbm_bytes": int(peak), "peak_hbm_gb": peak / 1e9,
+        "hbm_bytes": {"inputs": input_bytes, "selection": tensor_bytes(*sel),
+                      "attention_out": tensor_bytes(o), "workspace": int(ws.numel())},
+        "roofline": {
+            "kernel": "select_kernel (fused bf16 MFMA scoring + running top-k), the indexer "
+                      "stage of the step",
+            "bound": "mfma", "achieved": ix_flops / ix_s / 1e12, "peak": BF16_DENSE_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": ix_flops / ix_s / 1e12 / BF16_DENSE_PEAK_TFLOPS,
+            "traffic": None, "mean_launch_ms": ix_s * 1e3, "flops_per_step": ix_flops},
+        "attention": {
+            "kernel": "sparse_attention_kernel (gathered latents, bf16 MFMA, online softmax)",
+            "bound": "mfma", "achieved": at_flops / at_s / 1e12, "peak": BF16_DENSE_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": at_flops / at_s / 1e12 / BF16_DENSE_PEAK_TFLOPS,
+            "gathered_bytes": nsel * spec.D * 2,
+            "gather_gbps": nsel * spec.D * 2 / at_s / 1e9},
+    }
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        import oracle
+        rows = synth.sample_rows(spec, 4096, salt=100)
+        np.random.default_rng(100).shuffle(rows)
+        kcb = x["kc"].cpu().view(torch.int16).numpy().view(np.uint16)
+        kvb = kv.cpu().view(torch.int16).numpy().view(np.uint16)
+        done, pairs, n = 0.0, 0, 0
+        while rows and done < args.cpu_seconds:
+            r = rows.pop()
+            qb = x["q"][:, r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+            qab = qa[:, r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+            t1 = time.perf_counter()
+            oi, _ = oracle.indexer_topk(qb, kcb, x["w"][:, r:r + 1].cpu().numpy(), spec.m, spec.k,
+                                        q_pos0=r)
+            oracle.sparse_attention(qab, kvb, oi, oracle.default_scale(spec.D))
+            done += time.perf_counter() - t1
+            pairs += visible_pairs(1, spec.T, spec.m, q_pos0=r)
+            n += 1
+        rec["cpu_baseline"] = {
+            "value": pairs / done if done > 0 else 0.0, "unit": "pairs/s",
+            "cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model_name(),
+            "kind": "oracle",
+            "sample": f"{n} query rows, float64 oracle indexer + attention, {pairs} visible "
+                      f"pairs in {done:.1f} s"}
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -369,6 +480,8 @@ def main(argv=None):
     spec = synth.CONFIGS[WORKLOAD_SPEC.get(args.workload, args.workload)]
     if args.workload in TWO_STAGE:
         return bench_two_stage(args, spec, dev)
+    if args.workload in COMPOSE:
+        return bench_compose(args, spec, dev)
     fp8_q = args.workload in FP8_Q
     capacity = None
     if args.workload == "million" and args.mode == "bench":

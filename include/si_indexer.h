@@ -233,6 +233,27 @@ si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_
                              void* q8, float* w_eff, float* q_scale, void* stream);
 
 /*
+ * si_sparse_attention -- the attention consumer of the indexer's selection (StreamIndex
+ * abstract, aisoku.com page: a sparse attention kernel reads only the selected keys;
+ * jeff.news page, sequence diagram: merge-topk hands the key indices to the sparse
+ * attention).  The pages give no formula; reading used: per query row t and head h,
+ *     out[b,t,h,:] = sum_j softmax_j(scale * <qa[b,t,h,:], kv[b,s_j,:]>) * kv[b,s_j,:]
+ * over the row's selected entries s_j = idx[b,t,j] (the leading entries in [0, T); the
+ * first -1 or out-of-range index ends the row's list), the compressed latent serving
+ * as key and value for every head; a row with no entry outputs zeros.
+ *  qa  [B, S, HA, D] bf16, 16-byte aligned   kv [B, T, D] bf16, 16-byte aligned
+ *  idx [B, S, k] int32 (e.g. si_indexer_topk's out_idx)
+ *  out [B, S, HA, D] bf16, 8-byte aligned
+ * Arithmetic: logits by bf16 MFMA with fp32 accumulation, times scale * log2(e); exp2;
+ * running maximum and sum in fp32; the weights rounded to bf16 for the weight x value
+ * MFMA (fp32 accumulation); the output divided by the sum and rounded to bf16.
+ * D = 128, 1 <= HA <= 128, k >= 1.  Asynchronous on stream.
+ */
+si_status si_sparse_attention(const void* qa, const void* kv, const int32_t* idx, int64_t B,
+                              int64_t S, int64_t T, int32_t HA, int32_t D, int32_t k, float scale,
+                              void* out, void* stream);
+
+/*
  * ---- Two-stage (coarse -> fine) indexer --------------------------------------------
  * The candidate stage of the chengshu blog page "两级稀疏注意力：滑窗、压缩 KV latent 与
  * indexer", section "indexer：在摘要里做'预筛选'": blocks of `block` compressed keys are

@@ -19,6 +19,7 @@ from .api import (  # noqa: F401
     materialize_topk,
     plan,
     quantize_q,
+    sparse_attention,
     workspace,
     workspace_bytes,
 )
@@ -28,5 +29,5 @@ _lib.load()
 
 __all__ = [
     "Plan", "TwoStagePlan", "block_keys", "indexer_topk_two_stage", "two_stage_plan", "SiError", "indexer_topk", "indexer_select_chunk", "indexer_merge_chunk",
-    "materialize_scores", "materialize_topk", "plan", "quantize_q", "workspace", "workspace_bytes",
+    "materialize_scores", "materialize_topk", "plan", "quantize_q", "sparse_attention", "workspace", "workspace_bytes",
 ]

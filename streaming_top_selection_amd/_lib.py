@@ -56,6 +56,8 @@ SIGNATURES = {
     "si_indexer_merge_chunk": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _cfgp,
                                       _i32, _p, _p, _p, _sz, _p]),
     "si_quantize_q_e4m3": (_i32, [_p, _p, _i64, _i32, _i32, _p, _p, _p, _p]),
+    "si_sparse_attention": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_float,
+                                   _p, _p]),
     "si_block_keys_mean": (_i32, [_p, _i32, _i64, _i64, _i32, _i32, _p, _p]),
     "si_indexer_two_stage_plan": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _i64, _cfgp, ctypes.POINTER(SiTwoStagePlan)]),

@@ -279,3 +279,31 @@ def indexer_topk_two_stage(q, kc, kb, w, m: int, k: int, *, k_blocks: int = 2048
         q_pos0, ctypes.byref(cfg), _ptr(out[0]), _ptr(out[1]), _ptr(ws), ws.numel(),
         _stream(q.device)))
     return out
+
+
+# ---- sparse-attention consumer ---------------------------------------------------------
+
+def sparse_attention(qa, kv, idx, scale=None, *, out=None):
+    """si_sparse_attention: softmax attention of qa [B, S, HA, D] over the selected
+    compressed latents kv[b, idx[b, t, :]] (key = value), idx [B, S, k] int32 (-1 padded,
+    e.g. indexer_topk's indices).  scale defaults to 1/sqrt(D).  Returns bf16
+    [B, S, HA, D]."""
+    if qa.dim() != 4 or kv.dim() != 3 or idx.dim() != 3:
+        raise ValueError("expected qa [B,S,HA,D], kv [B,T,D], idx [B,S,k]")
+    B, S, HA, D = qa.shape
+    T = kv.shape[1]
+    if kv.shape[0] != B or kv.shape[2] != D or tuple(idx.shape[:2]) != (B, S):
+        raise ValueError("shape mismatch")
+    if qa.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or idx.dtype != torch.int32:
+        raise TypeError("qa and kv must be bfloat16, idx int32")
+    for name, t in (("qa", qa), ("kv", kv), ("idx", idx)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    k = idx.shape[2]
+    scale = 1.0 / (D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, S, HA, D), dtype=torch.bfloat16, device=qa.device)
+    lib = _lib.load()
+    _lib.check(lib.si_sparse_attention(_ptr(qa), _ptr(kv), _ptr(idx), B, S, T, HA, D, k,
+                                       ctypes.c_float(scale), _ptr(out), _stream(qa.device)))
+    return out

@@ -409,6 +409,38 @@ si_status si_quantize_q_e4m3(const void* q, const float* w, int64_t rows, int32_
     return SI_OK;
 }
 
+si_status si_sparse_attention(const void* qa, const void* kv, const int32_t* idx, int64_t B,
+                              int64_t S, int64_t T, int32_t HA, int32_t D, int32_t k, float scale,
+                              void* out, void* stream) {
+    g_last_error.clear();
+    if (B < 0 || S < 0 || T < 0) return fail(SI_ERR_INVALID_ARG, "B, S and T must be >= 0");
+    if (HA < 1 || k < 1 || D < 1) return fail(SI_ERR_INVALID_ARG, "HA, k and D must be >= 1");
+    if (D != si::kPlanD) return fail(SI_ERR_UNSUPPORTED, "only D = 128 is built");
+    if (HA > 128) return fail(SI_ERR_UNSUPPORTED, "HA must be <= 128");
+    if (T >= int64_t(0x7FFFFFFF)) return fail(SI_ERR_UNSUPPORTED, "T must be < 2^31 - 1");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SI_ERR_INVALID_ARG, "scale must be finite");
+    if (B == 0 || S == 0) return SI_OK;
+    if (!qa || !idx || !out || (T > 0 && !kv))
+        return fail(SI_ERR_INVALID_ARG, "qa, kv, idx and out must not be NULL");
+    if (!aligned(qa, 16) || (kv && !aligned(kv, 16)) || !aligned(idx, 4) || !aligned(out, 8))
+        return fail(SI_ERR_INVALID_ARG, "qa and kv must be 16-byte aligned, idx 4-byte, out 8-byte");
+    si::AttnArgs a;
+    a.qa = static_cast<const uint16_t*>(qa);
+    a.kv = static_cast<const uint16_t*>(kv);
+    a.idx = idx;
+    a.out = static_cast<uint16_t*>(out);
+    a.B = B;
+    a.S = S;
+    a.T = T;
+    a.HA = HA;
+    a.k = k;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = si::launch_sparse_attention(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sparse attention kernel launch");
+    return SI_OK;
+}
+
 si_status si_block_keys_mean(const void* kc, si_dtype kc_dtype, int64_t B, int64_t T, int32_t D,
                              int32_t block, void* kb, void* stream) {
     g_last_error.clear();

@@ -93,6 +93,18 @@ struct FineArgs {
     int32_t H, m, blk, k_blocks, k;
 };
 
+// Sparse attention over the selected compressed entries.
+struct AttnArgs {
+    const uint16_t* qa;    // [B, S, HA, kD] bf16 attention queries
+    const uint16_t* kv;    // [B, T, kD] bf16 compressed latents (key = value)
+    const int32_t* idx;    // [B, S, k] selected entries, -1 padded at the end
+    uint16_t* out;         // [B, S, HA, kD] bf16
+    int64_t B, S, T;
+    int32_t HA, k;
+    float scale_log2;      // softmax scale * log2(e)
+};
+
+hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_keys(const BlockKeyArgs& a, hipStream_t stream);
 hipError_t launch_fine_score(const FineArgs& a, hipStream_t stream);
 hipError_t launch_fine_select(const FineArgs& a, hipStream_t stream);

@@ -5,6 +5,7 @@ from .gen import (  # noqa: F401
     CONFIGS,
     InputSpec,
     duplicate_pairs,
+    gen_attention_inputs,
     gen_keys,
     gen_q_rows,
     gen_w_rows,

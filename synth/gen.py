@@ -24,7 +24,7 @@ import torch
 BLOCK_ROWS = 4096
 
 # tensor ids used in the seed mix
-_TID_Q, _TID_K, _TID_W, _TID_CQ, _TID_CK, _TID_DUP, _TID_ROWS = range(1, 8)
+_TID_Q, _TID_K, _TID_W, _TID_CQ, _TID_CK, _TID_DUP, _TID_ROWS, _TID_QA, _TID_KV = range(1, 10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -245,3 +245,22 @@ def sample_rows(spec: InputSpec, n: int, salt: int = 100):
     pick = torch.randperm(span, generator=g)[: max(0, min(n - 1, span))] + lo
     rows = sorted(set(pick.tolist()) | {spec.S - 1})
     return rows
+
+
+def gen_attention_inputs(spec: InputSpec, HA: int = 64, r0: int = 0, r1: Optional[int] = None,
+                         device="cpu"):
+    """Inputs of the sparse-attention consumer for query rows [r0, r1): attention queries
+    qa bf16 [B, r1 - r0, HA, D] and the compressed latents kv bf16 [B, T, D] (key =
+    value), both N(0, 1) rounded to bf16, drawn block by block like q."""
+    r1 = spec.S if r1 is None else r1
+    qa = torch.empty((spec.B, r1 - r0, HA, spec.D), dtype=torch.bfloat16, device=device)
+    kv = torch.empty((spec.B, spec.T, spec.D), dtype=torch.bfloat16, device=device)
+    for b in range(spec.B):
+        lo = r0
+        while lo < r1:
+            hi = min(r1, (lo // BLOCK_ROWS + 1) * BLOCK_ROWS)
+            qa[b, lo - r0:hi - r0] = _randn_rows(spec, _TID_QA, b, lo, hi, (HA, spec.D),
+                                                 device).to(torch.bfloat16)
+            lo = hi
+        kv[b] = _randn_rows(spec, _TID_KV, b, 0, spec.T, (spec.D,), device).to(torch.bfloat16)
+    return qa, kv
