@@ -77,7 +77,9 @@ CAPACITY_SLICE_ROWS = 16384
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["si_select.hpp", "si_select_inst.hip", "si_compact.hpp", "si_score.hpp",
                   "si_score_q8.hpp", "si_common.hpp"]
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_v4flash_s65536.md")
+PROFILE_SUMMARY = {"v4flash": os.path.join(ROOT, "profiles", "select_kernel_v4flash_s65536.md"),
+                   "v4flash-fp8": os.path.join(ROOT, "profiles",
+                                               "select_kernel_v4flash_fp8_s65536.md")}
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -90,12 +92,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per select launch from the committed counter summary, if it was taken
-    on the current kernel sources (else None: the counters no longer apply)."""
+def committed_traffic(workload="v4flash"):
+    """HBM bytes per select launch from the committed counter summary of the workload,
+    if it was taken on the current kernel sources (else None: the counters no longer
+    apply)."""
     try:
-        text = open(PROFILE_SUMMARY).read()
-    except OSError:
+        text = open(PROFILE_SUMMARY[workload]).read()
+    except (OSError, KeyError):
         return None
     m = re.search(r"<!-- traffic (\{.*?\}) -->", text)
     if not m:
@@ -618,8 +621,7 @@ def main(argv=None):
     peak_tflops = FP8_DENSE_PEAK_TFLOPS if fp8_q else BF16_DENSE_PEAK_TFLOPS
     q_dtype = "e4m3fn" if fp8_q else "bf16"
 
-    traffic = committed_traffic() if args.workload == "v4flash" and not any(knobs.values()) \
-        else None
+    traffic = committed_traffic(args.workload) if not any(knobs.values()) else None
     rec = {
         "metric": METRIC,
         "value": pairs / step_s,
@@ -766,7 +768,7 @@ def summarize(root, timed=5, workload="v4flash"):
     select-once), fetch/ and write/ (select-once counters) and copy_fetch/, copy_write/
     (copy-probe counters)."""
     import synth
-    spec = synth.CONFIGS[workload]
+    spec = synth.CONFIGS[WORKLOAD_SPEC.get(workload, workload)]
     flops = spec.B * visible_pairs(spec.S, spec.T, spec.m) * 2 * spec.H * spec.D
     stats = _kernel_stats(os.path.join(root, "trace"))
     sel = _pmc_value(os.path.join(root, "fetch"), "FETCH_SIZE", "select_kernel")
@@ -790,10 +792,11 @@ def summarize(root, timed=5, workload="v4flash"):
               f"{', '.join(f'{d / 1e3:.1f}' for _, d in disp)}")
         print(f"select_kernel over the {ts['launches']} timed launches (the last ones): "
               f"mean {ts['mean_us']:.1f} us, median {ts['median_us']:.1f} us")
-        frac = flops / (ts["mean_us"] * 1e-6) / (BF16_DENSE_PEAK_TFLOPS * 1e12)
+        peak = FP8_DENSE_PEAK_TFLOPS if workload in FP8_Q else BF16_DENSE_PEAK_TFLOPS
+        frac = flops / (ts["mean_us"] * 1e-6) / (peak * 1e12)
         print(f"roofline: {flops:.4e} algorithmic flop per launch / {ts['mean_us']:.1f} us = "
               f"{flops / (ts['mean_us'] * 1e-6) / 1e12:.1f} TFLOP/s = {frac:.3f} of the "
-              f"{BF16_DENSE_PEAK_TFLOPS:.0f} TFLOP/s bf16 dense peak")
+              f"{peak:.0f} TFLOP/s {'fp8' if workload in FP8_Q else 'bf16'} dense peak")
     gg = _pmc_value(os.path.join(root, "clock"), "GRBM_GUI_ACTIVE", "select_kernel")
     cd = _dispatches(os.path.join(root, "clock"), "select_kernel")
     if gg and cd:

@@ -35,14 +35,14 @@ def test_traffic_gate(tmp_path, monkeypatch):
            "write_bytes": 4.0, "bytes_per_launch": 7.0}
     good = tmp_path / "good.md"
     good.write_text(f"text\n<!-- traffic {json.dumps(rec)} -->\n")
-    monkeypatch.setattr(bench, "PROFILE_SUMMARY", str(good))
+    monkeypatch.setattr(bench, "PROFILE_SUMMARY", {"v4flash": str(good)})
     assert bench.committed_traffic() == rec
     stale = tmp_path / "stale.md"
     stale.write_text("<!-- traffic " + json.dumps(dict(rec, kernel_source_sha256_16="0" * 16))
                      + " -->\n")
-    monkeypatch.setattr(bench, "PROFILE_SUMMARY", str(stale))
+    monkeypatch.setattr(bench, "PROFILE_SUMMARY", {"v4flash": str(stale)})
     assert bench.committed_traffic() is None
-    monkeypatch.setattr(bench, "PROFILE_SUMMARY", str(tmp_path / "missing.md"))
+    monkeypatch.setattr(bench, "PROFILE_SUMMARY", {"v4flash": str(tmp_path / "missing.md")})
     assert bench.committed_traffic() is None
 
 
