@@ -113,7 +113,9 @@ si_status si_indexer_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D,
  * si_indexer_topk_workspace_bytes -- bytes of workspace si_indexer_topk needs for a
  * problem whose first q row is absolute position 0 (q_pos0 = 0) with the knobs cfg
  * (NULL = all automatic): the same value as si_indexer_plan(...).workspace_bytes.
- * The workspace holds one query chunk's candidate lists, so its size is bounded by
+ * The workspace holds one query chunk's candidate lists (plan.cand_capacity + 64 keys
+ * of 8 bytes per query and partition, a 4-byte count and a 16-byte keep rule), so its
+ * size is bounded by
  * the chunk, not by S (chunked partition-merge: skillsdirectory.com "Streamindex Csa
  * Topk", Implementation Steps 1-3).  A caller streaming q in slices with q_pos0 > 0
  * uses si_indexer_plan, whose plan depends on q_pos0.  Host only.
@@ -188,12 +190,16 @@ si_status si_indexer_topk_noalloc(const void* q, si_dtype q_dtype,
  * validation as si_indexer_topk; si_indexer_topk is exactly select(c) then merge(c)
  * for c = 0 .. n_chunks - 1, on the same stream and workspace.
  *
- * select: scores the chunk's query rows against their visible keys (bf16 MFMA, ReLU,
- *   head-weighted sum, mask) and keeps, per (query, key partition), the exact local
- *   top-k in the workspace (running threshold + candidate buffer, compacted by an
- *   exact radix select): the per-chunk candidates of the pages' data flow
- *   (jeff.news page, sequence diagram).
- * merge: merges each query's partition lists into the final sorted top-k rows of
+ * select: scores the chunk's query rows against their visible keys (MFMA, ReLU,
+ *   head-weighted sum, mask) and keeps, per (query, key partition), a candidate list
+ *   in the workspace that holds the exact local top-k: a running threshold, raised
+ *   after every key tile from a per-query score histogram, filters the scores, and a
+ *   compaction by exact radix select cuts a list that would overflow.  With one key
+ *   partition and k <= 512 the list is left holding its top k among at most
+ *   plan.cand_capacity keys, with a keep rule read off the histogram; otherwise each
+ *   list ends cut to exactly its top k.  These are the per-chunk candidates of the
+ *   pages' data flow (jeff.news page, sequence diagram).
+ * merge: cuts and merges each query's lists into the final sorted top-k rows of
  *   out_idx / out_score (the merge-topk step of the same diagram).
  */
 si_status si_indexer_select_chunk(const void* q, si_dtype q_dtype,

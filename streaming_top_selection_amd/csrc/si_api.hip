@@ -118,6 +118,8 @@ si_status run_select(const si::PlanInternal& pl, const si::Problem& P, int32_t k
     a.KP = pl.pub.key_partition;
     a.cand = static_cast<uint64_t*>(ws);
     a.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.cand_bytes);
+    a.defer_final = pl.defer_final ? 1 : 0;
+    a.rule = reinterpret_cast<si::KeepRule*>(static_cast<char*>(ws) + pl.rule_offset);
     const hipError_t e = si::launch_select(a, pl.nwave, pl.kb, pl.nsub, pl.pub.cand_capacity,
                                            op, stream);
     if (e != hipSuccess) return hip_fail(e, "select kernel launch");
@@ -149,6 +151,8 @@ si_status run_merge(const si::PlanInternal& pl, int64_t B, int64_t S, int64_t T,
     int32_t n2 = 1;
     while (n2 < k) n2 <<= 1;
     a.lds_entries = std::max<int32_t>(n2, a.P_chunk * k);
+    a.list_max = pl.defer_final ? pl.pub.cand_capacity : k;
+    a.rule = reinterpret_cast<const si::KeepRule*>(static_cast<const char*>(ws) + pl.rule_offset);
     const hipError_t e = si::launch_merge(a, stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return SI_OK;

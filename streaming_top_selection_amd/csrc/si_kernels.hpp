@@ -9,6 +9,22 @@
 
 namespace si {
 
+// Score bin of the select stage's per-query histogram: 256 bins linear in the score,
+// bin = fmaf(score, inv, off) clamped to [0, 255] (inv = 0: every key in bin 0).  The
+// select and merge kernels both call this, so they bin every key identically.
+__device__ __forceinline__ uint32_t hist_bin(float score, float inv, float off) {
+    return (uint32_t)__builtin_fminf(__builtin_fmaxf(__builtin_fmaf(score, inv, off), 0.0f), 255.0f);
+}
+
+// Keep rule of one list the select stage left for the merge to cut, read off the
+// query's histogram: the list's keys with hist_bin above d number `above` (< k), and
+// its top k are those plus the k - above largest keys of bin d.  d = -1: no rule.
+struct KeepRule {
+    int32_t d;
+    uint32_t above;
+    float inv, off;
+};
+
 // Select stage of one query chunk (fused score + running local top-k).
 struct SelectArgs {
     Problem P;
@@ -20,7 +36,10 @@ struct SelectArgs {
     int32_t QC;                       // row stride of the workspace (query_chunk)
     int64_t KP;                       // keys per partition
     uint64_t* cand;                   // [B][QC][P_ws][CG + kCandPad] selection keys
-    int32_t* cnt;                     // [B][QC][P_ws] list lengths (<= k when done)
+    int32_t* cnt;                     // [B][QC][P_ws] list lengths when done
+    int32_t defer_final;              // 1: lists end holding their top k among <= CG
+                                      // keys (the merge selects); 0: exactly their top k
+    KeepRule* rule;                   // [B][QC][P_ws] keep rules (written when deferred)
 };
 
 // Merge stage of one query chunk.
@@ -36,6 +55,9 @@ struct MergeArgs {
     int32_t* out_idx;
     float* out_score;
     int32_t lds_entries;              // dynamic LDS key slots of one merge group
+    int32_t list_max;                 // most keys a list holds: k, or the capacity when
+                                      // the select stage left the final selection here
+    const KeepRule* rule;             // [B][QC][P_ws] keep rules of such lists
 };
 
 // Materialise path: score write-out of rows [row0, row0 + rows).

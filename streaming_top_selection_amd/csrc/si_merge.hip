@@ -8,6 +8,7 @@
 // k keys, bounded by the planner to 8192) are gathered into LDS; if they hold more than k
 // keys an exact radix select finds the k-th key and an in-place compaction keeps the
 // top k; a bitonic sort orders them.  HBM traffic: read the lists, write the row.
+#include "si_compact.hpp"
 #include "si_kernels.hpp"
 #include "si_sort.hpp"
 
@@ -134,6 +135,120 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A
                           A.out_score + (b * A.S + row) * (int64_t)A.k, A.k, x, n, lane);
 }
 
+// ---- one partition per row, the final selection left to the merge --------------
+// The row's list holds its top k among up to 64*E keys (the select stage's threshold
+// keeps it short, but it did not cut it to k).  One wave per row: the list is loaded
+// into registers (E keys per lane).  The select stage's histogram gives the keep rule
+// (KeepRule): the keys above bin d, and the k - above largest of bin d, which are
+// gathered into LDS and ranked there.  A list the rule does not fit (a query whose
+// histogram was off, or more than 64 keys in bin d) has its k-th largest key found by
+// radix passes over the list in memory.
+// The k kept keys are gathered through LDS into the sort layout, sorted in registers
+// (64*EPL >= k) and written.  A list of at most k keys is sorted directly.
+template <int LE, int E>
+__global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(MergeArgs A) {
+    constexpr int EPL = 1 << LE;
+    __shared__ uint32_t hist[kSortWaves][256];
+    __shared__ __attribute__((aligned(16))) uint64_t stage[kSortWaves][64];
+    __shared__ __attribute__((aligned(16))) uint64_t kept[kSortWaves][64 * EPL];
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int64_t nrows = A.chunk_row1 - A.chunk_row0;
+    const int64_t id = (int64_t)blockIdx.x * kSortWaves + wave;
+    if (id >= A.B * nrows) return;
+    const int64_t b = id / nrows;
+    const int64_t r = id - b * nrows;
+    const int64_t row = A.chunk_row0 + r;
+    const int64_t slot0 = (b * A.QC + r) * A.P_ws;
+    const int64_t n_t = visible_keys(A.q_pos0 + row, A.m, A.T);
+    // the clamp keeps a corrupted count inside the list (the launcher checks that the
+    // list stride holds 64*E slots and that k <= 64*EPL)
+    const int n = __builtin_amdgcn_readfirstlane(n_t > 0 ? min(max(A.cnt[slot0], 0), 64 * E) : 0);
+    const int ne = (n + 63) / 64;                    // register slots e that hold keys
+    const uint64_t* src = A.cand + slot0 * (int64_t)A.CG;
+
+    uint64_t x[EPL];
+    int nk;
+    if (n <= A.k) {
+        // slots EPL*lane .. EPL*lane + EPL-1, as in merge_sort_kernel
+#pragma unroll
+        for (int e = 0; e < EPL; e += 2) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src + EPL * lane + e);
+            x[e] = ((uint64_t)v.y << 32) | v.x;
+            x[e + 1] = ((uint64_t)v.w << 32) | v.z;
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < n ? x[e] : 0ull;
+        nk = n;
+    } else {
+        // slots e >= ne hold no key: every pass below skips them (a uniform branch)
+        uint64_t v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = e < ne && e * 64 + lane < n ? src[e * 64 + lane] : 0ull;
+        // fast path, from the select stage's histogram: the keys above bin rl.d are
+        // kept (rl.above of them), and the k - above largest of bin rl.d, ranked in LDS
+        const KeepRule rl = A.rule[slot0];
+        bool fast = false;
+        uint64_t th = 0;
+        if (rl.d >= 0) {
+            stage[wave][lane] = 0ull;
+            int nhi = 0, nd = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (e < ne) {
+                    const bool valid = e * 64 + lane < n;
+                    const uint32_t bn = hist_bin(key_score(v[e]), rl.inv, rl.off);
+                    nhi += __popcll(__ballot(valid && bn > (uint32_t)rl.d));
+                    const bool eq = valid && bn == (uint32_t)rl.d;
+                    const uint64_t m = __ballot(eq);
+                    const int at = nd + (int)__builtin_amdgcn_mbcnt_hi(
+                                             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (eq && at < 64) stage[wave][at] = v[e];
+                    nd += __popcll(m);
+                }
+            }
+            const int need = A.k - (int)rl.above;
+            // the rule holds for this list (it always does; a list it does not fit goes
+            // the general way)
+            if (nhi == (int)rl.above && need >= 1 && need <= nd && nd <= 64) {
+                wave_sync();
+                th = stage_kth(stage[wave], nd, need);
+                fast = true;
+            }
+        }
+        // otherwise: the exact k-th largest key by radix passes over the list in memory
+        // (few registers, so the fast path keeps its occupancy)
+        if (!fast) th = wave_select_kth(LdsKeys{src, n}, A.k, hist[wave]);
+        // exactly k keys pass (keys are unique): gather them in order of slot
+        int base = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (e < ne) {
+                bool keep;
+                if (fast) {
+                    const uint32_t bn = hist_bin(key_score(v[e]), rl.inv, rl.off);
+                    keep = bn > (uint32_t)rl.d || (bn == (uint32_t)rl.d && v[e] >= th);
+                } else {
+                    keep = v[e] >= th;
+                }
+                keep = keep && e * 64 + lane < n;
+                const uint64_t m = __ballot(keep);
+                const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (keep && at < 64 * EPL) kept[wave][at] = v[e];   // at < k by construction
+                base += __popcll(m);
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < A.k ? kept[wave][EPL * lane + e] : 0ull;
+        nk = A.k;
+    }
+    sort_desc<LE>(x);
+    write_sorted_keys<LE>(A.out_idx + (b * A.S + row) * (int64_t)A.k,
+                          A.out_score + (b * A.S + row) * (int64_t)A.k, A.k, x, nk, lane);
+}
+
 // Several partitions whose lists hold at most 64*EPL keys together: gathered into LDS
 // (one 64-lane group per row, as in merge_kernel), then sorted in registers; the
 // first min(k, total) keys are the row's top-k.
@@ -184,9 +299,24 @@ static hipError_t launch_merge_sort(const MergeArgs& a, int64_t rows, hipStream_
     return hipGetLastError();
 }
 
+template <int LE, int E>
+static hipError_t launch_merge_select_sort(const MergeArgs& a, int64_t rows, hipStream_t stream) {
+    const int64_t grid = (rows + kSortWaves - 1) / kSortWaves;
+    hipLaunchKernelGGL((merge_select_sort_kernel<LE, E>), dim3((unsigned)grid),
+                       dim3(kSortWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     const int64_t rows = a.B * (a.chunk_row1 - a.chunk_row0);
     if (rows <= 0) return hipSuccess;
+    // one partition whose list may hold more than k keys: select, then sort
+    if (a.list_max > a.k) {
+        if (a.P_chunk != 1 || a.k > 512 || a.CG < a.list_max) return hipErrorInvalidValue;
+        if (a.list_max <= 2048) return launch_merge_select_sort<3, 32>(a, rows, stream);
+        if (a.list_max <= 4096) return launch_merge_select_sort<3, 64>(a, rows, stream);
+        return hipErrorInvalidValue;
+    }
     // one partition: sort the single list in registers (the list stride must hold the
     // network's 64*EPL slots, which every planned capacity does)
     if (a.P_chunk == 1) {

@@ -25,6 +25,8 @@ struct PlanInternal {
     int32_t nwave, kb, nsub;  // register tile = nwave * kb * 32 keys; key_tile = * nsub
     int64_t t_eff;            // keys visible to the last query row
     int64_t cand_bytes;       // offset of the count array in the workspace
+    int64_t rule_offset;      // offset of the keep-rule array (16 B per list)
+    bool defer_final;         // one partition, k <= 512: the merge selects the top k
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -82,10 +84,6 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
         default:
             msg = "key_tile must be 64, 128, 256, 512, 768 or 1024"; return SI_ERR_UNSUPPORTED;
     }
-    // candidate slots per (query, partition): room for k kept keys plus a key tile of
-    // arrivals with slack, and at least 2k so a compaction frees half the buffer
-    const int32_t cg = (2 * k <= 2048 && k + kt + 256 <= 2048) ? 2048 : 4096;
-
     const int64_t t_eff = (S == 0) ? 0 : visible_count_host(q_pos0 + S - 1, m, T);
     const int64_t q_tiles = B * ceil_div(S, kPlanTQ);
 
@@ -113,9 +111,19 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
               "partitions * k <= 8192): raise key_partition";
         return SI_ERR_UNSUPPORTED;
     }
+    // One partition and k <= 512: the select stage leaves each list holding its top k
+    // among at most 4096 keys, and the merge (many waves per SIMD) selects the k,
+    // instead of a final compaction in the MFMA kernel (one wave per SIMD).
+    pl.defer_final = nparts == 1 && k <= 512;
+    // candidate slots per (query, partition): room for k kept keys plus a key tile of
+    // arrivals with slack, and at least 2k so a compaction frees half the buffer; a
+    // deferred list gets 4096, so that with the histogram threshold most lists never
+    // compact before the partition's end
+    const int32_t cg =
+        (!pl.defer_final && 2 * k <= 2048 && k + kt + 256 <= 2048) ? 2048 : 4096;
 
     // query chunk
-    const int64_t per_row = B * nparts * (int64_t(cg + kPlanCandPad) * 8 + 4);
+    const int64_t per_row = B * nparts * (int64_t(cg + kPlanCandPad) * 8 + 4 + 16);
     int64_t qc;
     if (c.query_chunk) {
         qc = round_up(c.query_chunk, kPlanTQ);
@@ -129,6 +137,7 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
 
     const int64_t cand_bytes = round_up(B * qc * nparts * int64_t(cg + kPlanCandPad) * 8, 256);
     const int64_t cnt_bytes = round_up(B * qc * nparts * 4, 256);
+    const int64_t rule_bytes = round_up(B * qc * nparts * 16, 256);
 
     pl.pub.key_tile = kt;
     pl.pub.query_chunk = (int32_t)qc;
@@ -136,9 +145,10 @@ inline si_status make_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_t D
     pl.pub.n_partitions = (int32_t)nparts;
     pl.pub.n_chunks = (int32_t)nchunks;
     pl.pub.cand_capacity = cg;
-    pl.pub.workspace_bytes = (S == 0 || B == 0) ? 0 : cand_bytes + cnt_bytes;
+    pl.pub.workspace_bytes = (S == 0 || B == 0) ? 0 : cand_bytes + cnt_bytes + rule_bytes;
     pl.t_eff = t_eff;
     pl.cand_bytes = cand_bytes;
+    pl.rule_offset = cand_bytes + cnt_bytes;
     return SI_OK;
 }
 

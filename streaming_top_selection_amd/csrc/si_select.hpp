@@ -12,14 +12,26 @@
 //            workspace (CG slots): one LDS atomic per query and wave reserves a
 //            range, and each register writes its survivors as contiguous runs;
 // and after every key_tile keys (NSUB register tiles):
+//   refresh  the threshold of every query is raised from a histogram of its survivors
+//            kept in LDS (256 bins linear in the score between the extremes of the
+//            query's first key tile): the lower edge of the bin below the one holding
+//            the k-th best survivor, so at least k keys seen are above it;
 //   compact  a query whose buffer could overflow in the next key tile is reduced, by
 //            one wave with the keys in registers, to its best keys: between k and a
 //            little more than k mid-partition (whole score bins, see si_compact.hpp),
-//            exactly k at the partition's end; the smallest kept key's score becomes
-//            the threshold.
-// The merge stage then sorts (one partition) or merges the partition lists.
+//            exactly k at the partition's end unless the final selection is left to
+//            the merge (defer_final); the smallest kept key's score becomes the
+//            threshold if it is higher.
+// The merge stage then selects and sorts (one partition) or merges the partition lists.
 //
-// Correctness of the threshold: after a compaction the buffer holds the best keys
+// Correctness of the histogram threshold: a key in bin >= d (d >= 1) has
+// fmaf(s, inv, c) >= d, so its score exceeds lo + (d - 1) * width by nearly a whole
+// bin, which is more than the fp32 rounding of both sides as long as the bin width is
+// at least 2^-16 of the scores' magnitude (the histogram is switched off for a query
+// whose first key tile spans less).  The k keys in bins >= d are therefore strictly
+// above the new threshold, and a later key at or below it cannot enter the top-k.
+//
+// Correctness of the compaction threshold: after a compaction the buffer holds the best keys
 // seen so far, at least k of them, and the threshold key theta is the smallest kept
 // one; a later key below theta has k better keys already and can never enter the
 // top-k.  Keys are unique (score bits, ~index).  Every key compared with theta comes
@@ -56,7 +68,7 @@ __device__ __forceinline__ void compact_rows(uint64_t todo, uint64_t* cand_tile,
                                          keep_max, hist, stage, &tho);
         if (lane == 0) {
             sCnt[j] = kept;
-            sThf[j] = unord_f32(tho);
+            sThf[j] = fmaxf(sThf[j], unord_f32(tho));
         }
     };
     if constexpr (E <= 32) {
@@ -89,19 +101,28 @@ __device__ __forceinline__ void compact_rows(uint64_t todo, uint64_t* cand_tile,
 // kb holds the score of query q = mfma_row(r, lane) and key kbase + 32*kb + (lane & 31);
 // query q sits in register r_q = 4*(q/8) + q%4 of half (q/4)%2 of every block.
 // MASKED: the keys cross the end of some query's visible range (or of the partition).
+// Each survivor also counts in its query's score histogram (sRowHist, kHistStride
+// words per query, bins by hist_bin; inv = 0 puts every key in bin 0, which never moves
+// the threshold).  Every lane adds to the bin of its score, 1 for a survivor and 0
+// otherwise, so the atomics need no branch.
+constexpr int kHistStride = 260;   // 256 bins + 4 words, so rows start in different banks
+
 template <int KB, int CG, bool MASKED>
 __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t kbase,
                                               const float* sThf, const int32_t* sN,
-                                              int32_t* sCnt, uint64_t* cand_tile,
-                                              int64_t row_stride) {
+                                              int32_t* sCnt, const float* sInv,
+                                              const float* sOff, uint32_t* sRowHist,
+                                              uint64_t* cand_tile, int64_t row_stride) {
     const int lane = lane_id();
     const int il = lane & 31;
     const bool upper = lane >= 32;
-    float thf[16];
+    float thf[16], inv[16], off[16];
     int nj[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         thf[r] = sThf[mfma_row(r, lane)];
+        inv[r] = sInv[mfma_row(r, lane)];
+        off[r] = sOff[mfma_row(r, lane)];
         if constexpr (MASKED) nj[r] = sN[mfma_row(r, lane)];
     }
     auto passes = [&](int r, int kb) {
@@ -149,10 +170,13 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
         const int q_lo = mfma_row(r, 0), q_hi = mfma_row(r, 32);
         uint32_t next = sel((uint32_t)__builtin_amdgcn_readlane(my_base, q_hi),
                             (uint32_t)__builtin_amdgcn_readlane(my_base, q_lo));
-        uint64_t* const row = cand_tile + (int64_t)(upper ? q_hi : q_lo) * row_stride;
+        const int q = upper ? q_hi : q_lo;
+        uint64_t* const row = cand_tile + (int64_t)q * row_stride;
+        uint32_t* const hist = sRowHist + q * kHistStride;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const bool pass = passes(r, kb);
+            atomicAdd(&hist[hist_bin(acc[kb][r], inv[r], off[r])], pass ? 1u : 0u);
             const uint64_t m = __ballot(pass);
             const uint32_t m_lo = (uint32_t)m, m_hi = (uint32_t)(m >> 32);
             const uint32_t n_lo = (uint32_t)__popc(m_lo), n_hi = (uint32_t)__popc(m_hi);
@@ -164,6 +188,123 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
             row[dst] = ((uint64_t)ord_f32(acc[kb][r]) << 32) | low[kb];
             next += sel(n_hi, n_lo);
         }
+    }
+}
+
+// Extremes of the visible scores of each query in this register tile, folded into
+// sOmin / sOmax (score images, LDS atomics after a reduction over each half-wave).
+template <int KB>
+__device__ __forceinline__ void row_extremes(const f32x16 (&acc)[KB], int64_t kbase,
+                                             const int32_t* sN, uint32_t* sOmin,
+                                             uint32_t* sOmax) {
+    const int lane = lane_id();
+    const int il = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int q = mfma_row(r, lane);
+        const int n = sN[q];
+        uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            if (kbase + kb * kMB + il < n) {
+                const uint32_t o = ord_f32(acc[kb][r]);
+                lo = o < lo ? o : lo;
+                hi = o > hi ? o : hi;
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+            lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+        }
+        if (il == 0 && lo <= hi) {
+            atomicMin(&sOmin[q], lo);
+            atomicMax(&sOmax[q], hi);
+        }
+    }
+}
+
+// Histogram parameters of query row j from the extremes of its first key tile: 256
+// bins between them, or inv = 0 (histogram off) when the span is not finite or is
+// under 2^-8 of the scores' magnitude (then rounding could exceed a bin width).
+__device__ __forceinline__ void row_hist_params(uint32_t omin, uint32_t omax, float* lo,
+                                                float* wid, float* inv, float* off) {
+    *lo = 0.0f;
+    *wid = 0.0f;
+    *inv = 0.0f;
+    *off = 0.0f;
+    if (omin > omax) return;
+    const float a = unord_f32(omin), b = unord_f32(omax);
+    const float span = b - a;
+    const float mag = __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b));
+    if (!(span < __builtin_inff()) || !(span >= 0x1p-100f) || !(span >= mag * 0x1p-8f)) return;
+    *lo = a;
+    *wid = span * 0x1p-8f;
+    *inv = 256.0f / span;
+    *off = -(a * *inv);
+}
+
+// The bin d holding the k-th largest of the keys counted in query row j's histogram,
+// found by the LPR lanes of a group (lane sub = 0 .. LPR-1 holds bins 256 - BPL*(sub+1)
+// .. 256 - BPL*sub - 1, BPL = 256 / LPR, so sub 0 has the top bins): each lane sums
+// its bins (independent LDS reads), a scan over the group counts the keys above each
+// lane's range, and the lane where the count reaches k walks its bins from the top.
+// Returns true on that lane only, with *d and *above (the keys in bins above d).
+template <int LPR>
+__device__ __forceinline__ bool hist_group_kth(const uint32_t* hrow, int k, int sub, int* d,
+                                               uint32_t* above) {
+    constexpr int BPL = 256 / LPR;
+    const int b0 = 256 - BPL * (sub + 1);            // lowest bin of this lane
+    u32x4 h[BPL / 4];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPL / 4; ++i) {
+        h[i] = *reinterpret_cast<const u32x4*>(hrow + b0 + 4 * i);
+        sum += h[i].x + h[i].y + h[i].z + h[i].w;
+    }
+    // inclusive scan over the group, from sub = 0 (top bins) upward
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, o, LPR);
+        if (sub >= o) incl += t;
+    }
+    uint32_t cum = incl - sum;                       // keys in the bins above this lane's
+    if (!(cum < (uint32_t)k && incl >= (uint32_t)k)) return false;
+#pragma unroll
+    for (int i = BPL / 4 - 1; i >= 0; --i) {
+        const uint32_t b[4] = {h[i].w, h[i].z, h[i].y, h[i].x};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (cum + b[t] >= (uint32_t)k) {
+                *d = b0 + 4 * i + 3 - t;
+                *above = cum;
+                return true;
+            }
+            cum += b[t];
+        }
+    }
+    return false;   // not reached: the lane's bins hold the k-th key
+}
+
+// Raises the thresholds of query rows wave, wave + NWAVE, ... from their histograms
+// (64 / (kTQ / NWAVE) lanes per row): with d the bin holding the k-th best survivor,
+// every key in bins >= d is above lo + (d - 1) * width (see the file comment), so at
+// least k keys seen are.
+template <int NWAVE>
+__device__ __forceinline__ void refresh_thresholds(int k, const uint32_t* sRowHist,
+                                                   const float* sLo, const float* sWid,
+                                                   float* sThf) {
+    constexpr int RW = kTQ / NWAVE;                  // rows of this wave
+    constexpr int LPR = 64 / RW;                     // lanes per row
+    static_assert(RW * LPR == 64 && LPR >= 1 && 256 % (4 * LPR) == 0, "row groups");
+    const int lane = lane_id();
+    const int j = wave_id() + NWAVE * (lane / LPR);
+    int d;
+    uint32_t above;
+    if (hist_group_kth<LPR>(sRowHist + j * kHistStride, k, lane % LPR, &d, &above) && d >= 1) {
+        const float th = sLo[j] + (float)(d - 1) * sWid[j];
+        if (th > sThf[j]) sThf[j] = th;
     }
 }
 
@@ -184,6 +325,9 @@ select_kernel(SelectArgs A) {
     __shared__ int32_t sN[kTQ];            // end of the query's visible keys here
     __shared__ uint32_t sHist[NWAVE][256];
     __shared__ __attribute__((aligned(16))) uint64_t sStage[NWAVE][64];
+    __shared__ __attribute__((aligned(16))) uint32_t sRowHist[kTQ * kHistStride];   // survivors' bins
+    __shared__ float sLo[kTQ], sWid[kTQ], sInv[kTQ], sOff[kTQ];
+    __shared__ uint32_t sOmin[kTQ], sOmax[kTQ];
 
     const Problem& P = A.P;
     const int tid = threadIdx.x;
@@ -217,7 +361,11 @@ select_kernel(SelectArgs A) {
         sThf[tid] = tid < rows_valid ? -__builtin_inff() : __builtin_inff();
         sCnt[tid] = 0;
         sN[tid] = tid < rows_valid ? (int)min(visible_keys(t0 + tid, P.m, P.T), key_hi) : 0;
+        sOmin[tid] = ~0u;
+        sOmax[tid] = 0u;
     }
+    for (int i = tid; i < kTQ * kHistStride / 4; i += NT)
+        reinterpret_cast<u32x4*>(sRowHist)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // keys below this bound are visible to every row of the tile and inside the partition
     const int64_t all_visible = min(visible_keys(t0, P.m, P.T), key_hi);
@@ -232,20 +380,33 @@ select_kernel(SelectArgs A) {
 
         const int64_t kbase = key0 + (int64_t)wave * KB * kMB;
         uint64_t* const cand_tile = A.cand + slot0 * CGS;
+        if (key0 == key_lo) {
+            // the histogram scale of each query: the extremes of its first register tile
+            row_extremes<KB>(acc, kbase, sN, sOmin, sOmax);
+            __syncthreads();
+            if (tid < kTQ)
+                row_hist_params(sOmin[tid], sOmax[tid], &sLo[tid], &sWid[tid], &sInv[tid],
+                                &sOff[tid]);
+            __syncthreads();
+        }
         if (kbase + KB * kMB <= all_visible)
-            filter_append<KB, CG, false>(acc, kbase, sThf, sN, sCnt, cand_tile, row_stride);
+            filter_append<KB, CG, false>(acc, kbase, sThf, sN, sCnt, sInv, sOff, sRowHist,
+                                         cand_tile, row_stride);
         else
-            filter_append<KB, CG, true>(acc, kbase, sThf, sN, sCnt, cand_tile, row_stride);
+            filter_append<KB, CG, true>(acc, kbase, sThf, sN, sCnt, sInv, sOff, sRowHist,
+                                        cand_tile, row_stride);
 
         // ---- compaction: keep room for one more key tile; exact top-k at the end ----
         ++sub;
         const bool last = key0 + RT >= key_hi;
+        if (last && A.defer_final) break;   // the merge selects the top k of the list
         if (sub == NSUB || last) {
             sub = 0;
-            // every wave's reservations have landed once its LDS operations have: the
-            // counts are final, and every wave takes the same decision from them (no
-            // count changes before the barrier inside the branch)
+            // every wave's reservations and histogram counts have landed once its LDS
+            // operations have: the counts are final, and every wave takes the same
+            // decision from them (no count changes before the barrier inside the branch)
             lds_barrier();
+            if (!last) refresh_thresholds<NWAVE>(A.k, sRowHist, sLo, sWid, sThf);
             // mid-partition: make room for the next key tile, keeping at most keep_mid
             // keys (a few over k saves radix passes); at the end: exactly the top k
             const int limit = last ? A.k : CG - KT;
@@ -262,7 +423,27 @@ select_kernel(SelectArgs A) {
             }
         }
     }
-    if (tid < rows_valid) A.cnt[slot0 + (int64_t)tid * A.P_ws] = min(sCnt[tid], A.k);
+    // the last filter's reservations and histogram counts have landed before they are read
+    __syncthreads();
+    if (tid < rows_valid) A.cnt[slot0 + (int64_t)tid * A.P_ws] = min(sCnt[tid], A.defer_final ? CG : A.k);
+    if (A.defer_final) {
+        // the merge's keep rule of each row, from the histogram of every survivor (rows
+        // wave, wave + NWAVE, ...; the group lane that finds the k-th key's bin writes it)
+        constexpr int LPR = 64 / (kTQ / NWAVE);
+        const int j = wave + NWAVE * (lane / LPR);
+        int d = -1;
+        uint32_t above = 0u;
+        const bool found = hist_group_kth<LPR>(sRowHist + j * kHistStride, A.k, lane % LPR, &d, &above);
+        const bool none = __ballot(found) >> (lane / LPR * LPR) & ((1ull << LPR) - 1) ? false : true;
+        if (j < rows_valid && (found || (none && lane % LPR == 0))) {
+            KeepRule rl;
+            rl.inv = sInv[j];
+            rl.off = sOff[j];
+            rl.d = found && rl.inv > 0.0f ? d : -1;
+            rl.above = rl.d >= 0 ? above : 0u;
+            A.rule[slot0 + (int64_t)j * A.P_ws] = rl;
+        }
+    }
 }
 
 template <int NWAVE, int KB, int NSUB, int CG, int OP>

@@ -57,11 +57,12 @@ def plan(**kw):
 def test_plan_headline_workload_is_one_chunk_one_partition(lib):
     p = plan()
     assert p.n_chunks == 1 and p.query_chunk == 65536 and p.n_partitions == 1
-    assert p.key_tile == 512 and p.cand_capacity == 2048
-    # candidate keys (2048 slots + 64 pad slots per list) + counts for every query row,
-    # 256-byte aligned parts
-    assert p.workspace_bytes >= 65536 * (2048 + 64) * 8 + 65536 * 4
-    assert p.workspace_bytes < 65536 * (2048 + 64) * 8 + 65536 * 4 + 512
+    # one partition and k <= 512: the lists keep up to 4096 keys and the merge selects
+    assert p.key_tile == 512 and p.cand_capacity == 4096
+    # candidate keys (4096 slots + 64 pad slots per list) + counts + 16-byte keep rules
+    # for every query row, 256-byte aligned parts
+    need = 65536 * ((4096 + 64) * 8 + 4 + 16)
+    assert need <= p.workspace_bytes < need + 768
 
 
 def test_plan_million_token_workspace_is_bounded():
@@ -78,12 +79,21 @@ def test_plan_small_problems_split_keys_into_partitions():
     assert p.key_partition % p.key_tile == 0
 
 
-@pytest.mark.parametrize("kt,cg", [(64, 2048), (512, 2048), (768, 2048), (1024, 2048)])
-def test_plan_key_tiles(kt, cg):
+@pytest.mark.parametrize("kt", [64, 512, 768, 1024])
+def test_plan_key_tiles(kt):
     p = plan(key_tile=kt)
-    assert p.key_tile == kt and p.cand_capacity == cg
+    assert p.key_tile == kt and p.cand_capacity == 4096
     # the buffer always has room for k kept keys plus one key tile of arrivals
     assert p.cand_capacity - p.key_tile > 512
+
+
+@pytest.mark.parametrize("kt,cg", [(64, 2048), (512, 2048), (768, 2048), (1024, 2048)])
+def test_plan_key_tiles_with_partitions(kt, cg):
+    # several key partitions: each list ends cut to its exact top k
+    p = plan(S=8192, T=8192, m=1, k=64, key_tile=kt, key_partition=4 * kt)
+    assert p.n_partitions > 1
+    assert p.key_tile == kt and p.cand_capacity == cg
+    assert p.cand_capacity - p.key_tile > 64
 
 
 def test_plan_large_k_gets_the_large_buffer():
