@@ -11,7 +11,8 @@
 //            the survivors are appended to the query's candidate buffer in the
 //            workspace (CG slots): one LDS atomic per query and wave reserves a
 //            range, and each register writes its survivors as contiguous runs;
-// and after every key_tile keys (NSUB register tiles):
+// and after every key_tile keys (NSUB register tiles; after the fourth key tile of a
+// partition, every fourth):
 //   refresh  the threshold of every query is raised from a histogram of its survivors
 //            kept in LDS (256 bins linear in the score between the extremes of the
 //            query's first key tile): the lower edge of the bin below the one holding
@@ -107,6 +108,12 @@ __device__ __forceinline__ void compact_rows(uint64_t todo, uint64_t* cand_tile,
 // otherwise, so the atomics need no branch.
 constexpr int kHistStride = 260;   // 256 bins + 4 words, so rows start in different banks
 
+// buffer_store_dwordx2: 8 bytes to rsrc.base + voffset (32-bit per-lane offsets, the
+// base in scalar registers).
+extern "C" __device__ void si_raw_buffer_store_v2i32(u32x2 vdata, i32x4 rsrc, int voffset,
+                                                      int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v2i32");
+
 template <int KB, int CG, bool MASKED>
 __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t kbase,
                                               const float* sThf, const int32_t* sN,
@@ -165,13 +172,17 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) low[kb] = ~(uint32_t)(kbase + kb * kMB + il);
     const uint32_t pad = (uint32_t)CG | (uint32_t)il;
+    // the tile's lists through one buffer resource: 32-bit offsets (32 lists of at most
+    // 64 partitions x (CG + 64) keys stay far below 4 GiB)
+    const i32x4 rsrc = make_rsrc(reinterpret_cast<uint64_t>(cand_tile), 0xFFFFFFFFu);
+    const uint32_t row_bytes = (uint32_t)row_stride * 8u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int q_lo = mfma_row(r, 0), q_hi = mfma_row(r, 32);
         uint32_t next = sel((uint32_t)__builtin_amdgcn_readlane(my_base, q_hi),
                             (uint32_t)__builtin_amdgcn_readlane(my_base, q_lo));
         const int q = upper ? q_hi : q_lo;
-        uint64_t* const row = cand_tile + (int64_t)q * row_stride;
+        const uint32_t row_off = (uint32_t)q * row_bytes;   // this lane's list in the tile
         uint32_t* const hist = sRowHist + q * kHistStride;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -185,7 +196,8 @@ __device__ __forceinline__ void filter_append(const f32x16 (&acc)[KB], int64_t k
             // the compaction policy keeps every position below CG; the clamp only
             // keeps a broken invariant inside this query's pad slots
             const uint32_t dst = min(pass ? next + rank : ~0u, pad);
-            row[dst] = ((uint64_t)ord_f32(acc[kb][r]) << 32) | low[kb];
+            si_raw_buffer_store_v2i32(u32x2{low[kb], ord_f32(acc[kb][r])}, rsrc,
+                                      (int)(row_off + 8u * dst), 0, 0);
             next += sel(n_hi, n_lo);
         }
     }
@@ -374,6 +386,7 @@ select_kernel(SelectArgs A) {
     const int keep_mid = A.k + (CG - KT - A.k) / 4;
 
     int sub = 0;
+    int key_tiles = 0;                     // key tiles done in this partition
     for (int64_t key0 = key_lo; key0 < key_hi; key0 += RT) {
         f32x16 acc[KB];
         score_tile<NWAVE, KB, OP>(P, b, row0, rows_valid, key0, key_hi, L, Q, acc);
@@ -406,7 +419,11 @@ select_kernel(SelectArgs A) {
             // operations have: the counts are final, and every wave takes the same
             // decision from them (no count changes before the barrier inside the branch)
             lds_barrier();
-            if (!last) refresh_thresholds<NWAVE>(A.k, sRowHist, sLo, sWid, sThf);
+            // the threshold moves most in the first key tiles: refresh after each of the
+            // first four, then after every fourth
+            ++key_tiles;
+            if (!last && (key_tiles <= 4 || (key_tiles & 3) == 0))
+                refresh_thresholds<NWAVE>(A.k, sRowHist, sLo, sWid, sThf);
             // mid-partition: make room for the next key tile, keeping at most keep_mid
             // keys (a few over k saves radix passes); at the end: exactly the top k
             const int limit = last ? A.k : CG - KT;
