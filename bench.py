@@ -331,6 +331,25 @@ def bench_compose(args, spec, dev):
     return 0
 
 
+def list_lengths(si, spec, pl, ws, qop, x, knobs):
+    """Keys the select stage leaves in the lists of every query row (summed over the
+    query chunks: one more select launch per chunk, each list count read back)."""
+    import numpy as np
+    import torch
+    nrows_ws = spec.B * pl.query_chunk * pl.n_partitions
+    cand_bytes = -(-nrows_ws * (pl.cand_capacity + 64) * 8 // 256) * 256
+    total = 0
+    for c in range(pl.n_chunks):
+        si.indexer_select_chunk(qop[0], x["kc"], qop[1], spec.m, spec.k, c, ws,
+                                kc_scale=x["kc_scale"], **knobs)
+        torch.cuda.synchronize()
+        rows = min(spec.S, (c + 1) * pl.query_chunk) - c * pl.query_chunk
+        cnt = ws[cand_bytes:cand_bytes + nrows_ws * 4].view(torch.int32).cpu().numpy()
+        cnt = cnt.reshape(spec.B, pl.query_chunk, pl.n_partitions)[:, :rows]
+        total += int(np.minimum(np.maximum(cnt, 0), pl.cand_capacity).sum())
+    return total
+
+
 def cpu_model_name():
     """The host CPU's model name (lscpu), or /proc/cpuinfo's, or "unknown"."""
     import subprocess
@@ -574,6 +593,9 @@ def main(argv=None):
     torch.cuda.synchronize(dev)
     assert torch.equal(ref[0], out[0]) and torch.equal(ref[1], out[1])
     del ref
+    # the keys the select stage leaves per list (for the merge's bytes), before the
+    # warm-up so that the timed launches stay the last ones
+    list_keys = list_lengths(si, spec, pl, ws, qop, x, knobs)
     if capacity is not None:
         assert torch.equal(capacity_outputs[0], out[0]) and \
             torch.equal(capacity_outputs[1], out[1]), "streamed-q run differs"
@@ -611,12 +633,12 @@ def main(argv=None):
     sel_step_s = sum(sel_ms) / args.steps / 1e3
     mrg_step_s = sum(mrg_ms) / args.steps / 1e3
     achieved_tflops = flops / sel_step_s / 1e12
-    # merge: read every query's kept list (min(k, n_t) keys of 8 B, one partition
-    # each when n_partitions == 1) and its count, write k (idx, score) pairs per row
+    # merge: read every list the select stage left (its keys of 8 B, its count and its
+    # 16-byte keep rule), write k (idx, score) pairs per row; the list lengths were read
+    # back after one more select launch per chunk, outside the timed region
     import numpy as np
-    t = np.arange(spec.S, dtype=np.int64)
-    kept = int(np.minimum(spec.k, np.minimum(spec.T, (t + 1) // spec.m)).sum()) * spec.B
-    merge_bytes = kept * 8 + spec.B * spec.S * pl.n_partitions * 4 + spec.B * spec.S * spec.k * 8
+    merge_bytes = (list_keys * 8 + spec.B * spec.S * pl.n_partitions * (4 + 16)
+                   + spec.B * spec.S * spec.k * 8)
     merge_gbps = merge_bytes / mrg_step_s / 1e9
     peak_tflops = FP8_DENSE_PEAK_TFLOPS if fp8_q else BF16_DENSE_PEAK_TFLOPS
     q_dtype = "e4m3fn" if fp8_q else "bf16"
@@ -664,12 +686,15 @@ def main(argv=None):
             "flops_per_step": flops,
         },
         "merge": {
-            "kernel": ("merge_sort_kernel (one list per row, register bitonic sort)"
-                       if pl.n_partitions == 1 and spec.k <= 2048
+            "kernel": ("merge_select_sort_kernel (keep rule from the select histogram, "
+                       "register bitonic sort)" if pl.n_partitions == 1 and spec.k <= 512
+                       else "merge_sort_kernel (one list per row, register bitonic sort)"
+                       if pl.n_partitions == 1
                        else "merge_kernel (LDS gather, select, bitonic sort)"),
             "bound": "hbm", "achieved": merge_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": merge_gbps / HBM_PEAK_GBPS,
             "mean_launch_ms": mrg_mean_s * 1e3, "bytes_per_step": merge_bytes,
+            "list_keys_per_row": list_keys / (spec.B * spec.S),
         },
     }
     if fp8_q:
