@@ -54,7 +54,15 @@ WORKLOADS["long-two-stage"] = (
     "Two-stage indexer at the long-context shape: B=1, S=262144, m=4, T=65536, H_I=64, D=128; "
     "block keys = bf16 mean of 8 keys, coarse top-2048 blocks, fine top-512 of their keys "
     "(+ the trailing incomplete block), bf16")
-TWO_STAGE = {"long-two-stage": dict(block=8, k_blocks=2048)}
+WORKLOADS["million-bf16"] = (
+    "Million-token shape with bf16 keys: B=1, S=1048576, m=4, T=262144, H_I=64, D=128, "
+    "top-k=512, bf16 q/k (the single-stage reference for million-two-stage)")
+WORKLOADS["million-two-stage"] = (
+    "Two-stage indexer at the million-token shape: B=1, S=1048576, m=4, T=262144, H_I=64, "
+    "D=128; block keys = bf16 mean of 8 keys, coarse top-2048 blocks, fine top-512 of their "
+    "keys (+ the trailing incomplete block), bf16")
+TWO_STAGE = {"long-two-stage": dict(block=8, k_blocks=2048),
+             "million-two-stage": dict(block=8, k_blocks=2048)}
 WORKLOADS["compose-long"] = (
     "Indexer composed with the sparse-attention consumer at the long-context shape: B=1, "
     "S=262144, m=4, T=65536, H_I=64, D=128, top-k=512 (streaming indexer), then softmax "
@@ -63,13 +71,14 @@ WORKLOADS["compose-long"] = (
 COMPOSE = {"compose-long": dict(HA=64)}
 # workload -> input configuration (synth.CONFIGS); the fp8-q workloads quantise q in the step
 WORKLOAD_SPEC = {"v4flash-fp8": "v4flash-e4m3", "v4flash-mxfp4": "v4flash-mxfp4",
-                 "long-two-stage": "long", "compose-long": "long"}
+                 "long-two-stage": "long", "compose-long": "long",
+                 "million-two-stage": "million-bf16"}
 FP8_Q = {"v4flash-fp8", "v4flash-mxfp4"}
 DTYPE_NAME = {("bf16", "bf16"): "bf16", ("bf16", "e4m3fn"): "bf16",
               ("e4m3fn", "e4m3fn"): "e4m3", ("e4m3fn", "mxfp4"): "e4m3xe2m1"}
 # default (steps, warmup) per workload: about a minute of timed work at most
 DEFAULT_STEPS = {"long": (5, 1), "million": (3, 1), "long-two-stage": (5, 1),
-                 "compose-long": (5, 1)}
+                 "compose-long": (5, 1), "million-bf16": (3, 1), "million-two-stage": (3, 1)}
 # q rows per slice of the million workload's streamed-q capacity pass
 CAPACITY_SLICE_ROWS = 16384
 

@@ -57,6 +57,8 @@ CONFIGS = {
     "long": InputSpec(B=1, S=262144, T=65536, k=512, seed=4),
     # Million-token capacity run with E4M3 keys and a per-row fp32 scale.
     "million": InputSpec(B=1, S=1048576, T=262144, k=512, seed=5, kc_dtype="e4m3fn"),
+    # The million-token shape with bf16 keys (single-stage against two-stage indexer).
+    "million-bf16": InputSpec(B=1, S=1048576, T=262144, k=512, seed=5),
     # The V4-Flash layer with low-precision keys (the fp8-q paths quantise q themselves).
     "v4flash-e4m3": InputSpec(B=1, S=65536, T=16384, k=512, seed=3, channel_scale=(0.5, 2.0),
                               kc_dtype="e4m3fn"),
