@@ -136,16 +136,17 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A
 }
 
 // ---- one partition per row, the final selection left to the merge --------------
-// The row's list holds its top k among up to 64*E keys (the select stage's threshold
-// keeps it short, but it did not cut it to k).  One wave per row: the list is loaded
-// into registers (E keys per lane).  The select stage's histogram gives the keep rule
-// (KeepRule): the keys above bin d, and the k - above largest of bin d, which are
-// gathered into LDS and ranked there.  A list the rule does not fit (a query whose
-// histogram was off, or more than 64 keys in bin d) has its k-th largest key found by
-// radix passes over the list in memory.
-// The k kept keys are gathered through LDS into the sort layout, sorted in registers
-// (64*EPL >= k) and written.  A list of at most k keys is sorted directly.
-template <int LE, int E>
+// The row's list holds its top k among up to list_max keys (the select stage's
+// threshold keeps it short, but it did not cut it to k).  One wave per row streams the
+// list once, 64 keys a round: the select stage's histogram gives the keep rule
+// (KeepRule), so a key above bin d goes straight to the kept set in LDS and a key of
+// bin d to a 64-slot stage, where the k - above largest are found by counting larger
+// keys.  A list the rule does not fit (a query whose histogram was off, or more than
+// 64 keys in bin d) has its k-th largest key found by radix passes over the list in
+// memory and is streamed again.  The k kept keys are read back from LDS in the sort
+// layout, sorted in registers (64*EPL >= k) and written.  A list of at most k keys is
+// sorted directly.  Few registers per wave, so many waves per SIMD hide the loads.
+template <int LE>
 __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(MergeArgs A) {
     constexpr int EPL = 1 << LE;
     __shared__ uint32_t hist[kSortWaves][256];
@@ -162,9 +163,8 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
     const int64_t slot0 = (b * A.QC + r) * A.P_ws;
     const int64_t n_t = visible_keys(A.q_pos0 + row, A.m, A.T);
     // the clamp keeps a corrupted count inside the list (the launcher checks that the
-    // list stride holds 64*E slots and that k <= 64*EPL)
-    const int n = __builtin_amdgcn_readfirstlane(n_t > 0 ? min(max(A.cnt[slot0], 0), 64 * E) : 0);
-    const int ne = (n + 63) / 64;                    // register slots e that hold keys
+    // list stride holds list_max slots and that k <= 64*EPL)
+    const int n = __builtin_amdgcn_readfirstlane(n_t > 0 ? min(max(A.cnt[slot0], 0), A.list_max) : 0);
     const uint64_t* src = A.cand + slot0 * (int64_t)A.CG;
 
     uint64_t x[EPL];
@@ -181,67 +181,57 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
         for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < n ? x[e] : 0ull;
         nk = n;
     } else {
-        // slots e >= ne hold no key: every pass below skips them (a uniform branch)
-        uint64_t v[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = e < ne && e * 64 + lane < n ? src[e * 64 + lane] : 0ull;
-        // fast path, from the select stage's histogram: the keys above bin rl.d are
-        // kept (rl.above of them), and the k - above largest of bin rl.d, ranked in LDS
+        uint64_t* const kw = kept[wave];
+        uint64_t* const sw = stage[wave];
+        // appends the keys of `keep` (one per lane) at base, in lane order
+        auto append = [&](bool keep, uint64_t v, uint64_t* dst, int cap, int& base) {
+            const uint64_t m = __ballot(keep);
+            const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (keep && at < cap) dst[at] = v;
+            base += __popcll(m);
+        };
         const KeepRule rl = A.rule[slot0];
-        bool fast = false;
-        uint64_t th = 0;
-        if (rl.d >= 0) {
-            stage[wave][lane] = 0ull;
-            int nhi = 0, nd = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (e < ne) {
-                    const bool valid = e * 64 + lane < n;
-                    const uint32_t bn = hist_bin(key_score(v[e]), rl.inv, rl.off);
-                    nhi += __popcll(__ballot(valid && bn > (uint32_t)rl.d));
-                    const bool eq = valid && bn == (uint32_t)rl.d;
-                    const uint64_t m = __ballot(eq);
-                    const int at = nd + (int)__builtin_amdgcn_mbcnt_hi(
-                                             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    if (eq && at < 64) stage[wave][at] = v[e];
-                    nd += __popcll(m);
-                }
+        bool fast = rl.d >= 0;
+        int base = 0;
+        if (fast) {
+            sw[lane] = 0ull;
+            int nd = 0;
+            const uint32_t d = (uint32_t)rl.d;
+#pragma unroll 4
+            for (int i = 0; i < n; i += 64) {
+                const int slot = i + lane;
+                const uint64_t v = slot < n ? src[slot] : 0ull;
+                const uint32_t bn = hist_bin(key_score(v), rl.inv, rl.off);
+                append(slot < n && bn > d, v, kw, 64 * EPL, base);
+                append(slot < n && bn == d, v, sw, 64, nd);
             }
-            const int need = A.k - (int)rl.above;
+            const int need = A.k - base;
             // the rule holds for this list (it always does; a list it does not fit goes
             // the general way)
-            if (nhi == (int)rl.above && need >= 1 && need <= nd && nd <= 64) {
+            fast = base == (int)rl.above && need >= 1 && need <= nd && nd <= 64;
+            if (fast) {
                 wave_sync();
-                th = stage_kth(stage[wave], nd, need);
-                fast = true;
+                const uint64_t th = stage_kth(sw, nd, need);
+                const uint64_t v = sw[lane];
+                append(lane < nd && v >= th, v, kw, 64 * EPL, base);
             }
         }
-        // otherwise: the exact k-th largest key by radix passes over the list in memory
-        // (few registers, so the fast path keeps its occupancy)
-        if (!fast) th = wave_select_kth(LdsKeys{src, n}, A.k, hist[wave]);
-        // exactly k keys pass (keys are unique): gather them in order of slot
-        int base = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if (e < ne) {
-                bool keep;
-                if (fast) {
-                    const uint32_t bn = hist_bin(key_score(v[e]), rl.inv, rl.off);
-                    keep = bn > (uint32_t)rl.d || (bn == (uint32_t)rl.d && v[e] >= th);
-                } else {
-                    keep = v[e] >= th;
-                }
-                keep = keep && e * 64 + lane < n;
-                const uint64_t m = __ballot(keep);
-                const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                if (keep && at < 64 * EPL) kept[wave][at] = v[e];   // at < k by construction
-                base += __popcll(m);
+        if (!fast) {
+            // the exact k-th largest key by radix passes over the list in memory, then
+            // the keys at or above it (exactly k: keys are unique)
+            const uint64_t th = wave_select_kth(LdsKeys{src, n}, A.k, hist[wave]);
+            base = 0;
+#pragma unroll 4
+            for (int i = 0; i < n; i += 64) {
+                const int slot = i + lane;
+                const uint64_t v = slot < n ? src[slot] : 0ull;
+                append(slot < n && v >= th, v, kw, 64 * EPL, base);
             }
         }
         wave_sync();
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < A.k ? kept[wave][EPL * lane + e] : 0ull;
+        for (int e = 0; e < EPL; ++e) x[e] = EPL * lane + e < A.k ? kw[EPL * lane + e] : 0ull;
         nk = A.k;
     }
     sort_desc<LE>(x);
@@ -299,10 +289,10 @@ static hipError_t launch_merge_sort(const MergeArgs& a, int64_t rows, hipStream_
     return hipGetLastError();
 }
 
-template <int LE, int E>
+template <int LE>
 static hipError_t launch_merge_select_sort(const MergeArgs& a, int64_t rows, hipStream_t stream) {
     const int64_t grid = (rows + kSortWaves - 1) / kSortWaves;
-    hipLaunchKernelGGL((merge_select_sort_kernel<LE, E>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((merge_select_sort_kernel<LE>), dim3((unsigned)grid),
                        dim3(kSortWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -312,10 +302,9 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     // one partition whose list may hold more than k keys: select, then sort
     if (a.list_max > a.k) {
-        if (a.P_chunk != 1 || a.k > 512 || a.CG < a.list_max) return hipErrorInvalidValue;
-        if (a.list_max <= 2048) return launch_merge_select_sort<3, 32>(a, rows, stream);
-        if (a.list_max <= 4096) return launch_merge_select_sort<3, 64>(a, rows, stream);
-        return hipErrorInvalidValue;
+        if (a.P_chunk != 1 || a.k > 512 || a.CG < a.list_max || a.CG < 512)
+            return hipErrorInvalidValue;
+        return launch_merge_select_sort<3>(a, rows, stream);
     }
     // one partition: sort the single list in registers (the list stride must hold the
     // network's 64*EPL slots, which every planned capacity does)
