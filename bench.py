@@ -340,6 +340,33 @@ def bench_compose(args, spec, dev):
     return 0
 
 
+def gemm_ceiling():
+    """The dense bf16 MFMA rate a library GEMM (torch -> hipBLASLt) reaches on this GPU,
+    square n x n x n products of N(0,1) data: the practical ceiling the select kernel's
+    fraction of the nominal peak is read against."""
+    import torch
+    dev = torch.device("cuda", 0)
+    rec = {}
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            a @ b
+        torch.cuda.synchronize(dev)
+        reps = 20 if n < 16384 else 6
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            a @ b
+        e1.record()
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2 * n ** 3 / ms / 1e9
+        rec[str(n)] = {"ms": ms, "tflops": tf, "frac_of_bf16_peak": tf / BF16_DENSE_PEAK_TFLOPS}
+    print(json.dumps({"gemm_ceiling_bf16": rec}), flush=True)
+    return 0
+
+
 def list_lengths(si, spec, pl, ws, qop, x, knobs):
     """Keys the select stage leaves in the lists of every query row (summed over the
     query chunks: one more select launch per chunk, each list count read back)."""
@@ -482,7 +509,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "select-once", "copy-probe",
-                                                         "summarize"],
+                                                         "summarize", "gemm-ceiling"],
                     help="select-once / copy-probe: single launches for rocprofv3 counter "
                          "runs; summarize DIR: turn rocprofv3 CSV output into the summary")
     ap.add_argument("--dir", default=None, help="rocprofv3 output root for --mode summarize")
@@ -494,6 +521,8 @@ def main(argv=None):
     args.warmup = d_warm if args.warmup is None else args.warmup
     if args.mode == "summarize":
         return summarize(args.dir, args.timed_launches, args.workload)
+    if args.mode == "gemm-ceiling":
+        return gemm_ceiling()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
