@@ -509,7 +509,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "select-once", "copy-probe",
-                                                         "summarize", "gemm-ceiling"],
+                                                         "summarize", "gemm-ceiling",
+                                                         "kernel-table"],
                     help="select-once / copy-probe: single launches for rocprofv3 counter "
                          "runs; summarize DIR: turn rocprofv3 CSV output into the summary")
     ap.add_argument("--dir", default=None, help="rocprofv3 output root for --mode summarize")
@@ -523,6 +524,8 @@ def main(argv=None):
         return summarize(args.dir, args.timed_launches, args.workload)
     if args.mode == "gemm-ceiling":
         return gemm_ceiling()
+    if args.mode == "kernel-table":
+        return kernel_table(args.dir)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -799,6 +802,20 @@ def _kernel_stats(csv_dir):
         with open(path) as f:
             rows += list(csv.DictReader(f))
     return rows
+
+
+def kernel_table(root):
+    """The library's kernels in a rocprofv3 --kernel-trace --stats run under root: calls,
+    total and mean duration (torch's own kernels left out)."""
+    rows = [r for r in _kernel_stats(root) if "si::" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print("| kernel | calls | total ms | mean us |")
+    print("|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].replace("void ", "").split("(")[0]
+        print(f"| {name} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+              f"{float(r['AverageNs']) / 1e3:.1f} |")
+    return 0
 
 
 def _dispatches(csv_dir, kernel_substr):

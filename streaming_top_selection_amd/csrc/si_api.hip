@@ -174,10 +174,15 @@ si_status run_indexer(const si::PlanInternal& pl, const si::Problem& P, int32_t 
 // ---- two-stage plan ---------------------------------------------------------------
 struct TwoStagePlan {
     int64_t qc, n_chunks, cand_stride;
+    int64_t cqc;                 // coarse chunk: query rows of one coarse indexer call
     int64_t coarse_ws, cidx_off, cscore_off, cand_off, total;
 };
 
 constexpr int64_t kTwoStageAutoChunk = 4096;
+// The coarse stage runs over several fine chunks at once (about this many rows), so
+// that its query tiles fill the chip without key partitions and its merge stays a
+// register sort.
+constexpr int64_t kTwoStageCoarseRows = 32768;
 
 si_config coarse_config(const si_config* cfg) {
     si_config c = cfg ? *cfg : si_config{0, 0, 0, 0};
@@ -205,11 +210,14 @@ si_status make_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_
     tp.qc = qc;
     tp.n_chunks = (S == 0 || B == 0) ? 0 : si::ceil_div(S, qc);
     tp.cand_stride = si::round_up((int64_t)blk * k_blocks + blk, 64);
-    // the coarse workspace of the widest chunk plan
+    tp.cqc = std::min<int64_t>(std::max<int64_t>(S, 1),
+                               qc * std::max<int64_t>(1, kTwoStageCoarseRows / qc));
+    // the coarse workspace of the widest coarse-chunk plan
     const si_config cc = coarse_config(cfg);
     tp.coarse_ws = 0;
-    for (int64_t c = 0; c < tp.n_chunks; ++c) {
-        const int64_t r0 = c * qc, rows = std::min(qc, S - r0);
+    const int64_t n_coarse = (S == 0 || B == 0) ? 0 : si::ceil_div(S, tp.cqc);
+    for (int64_t c = 0; c < n_coarse; ++c) {
+        const int64_t r0 = c * tp.cqc, rows = std::min(tp.cqc, S - r0);
         si::PlanInternal pl;
         st = si::make_plan(1, rows, T / blk, H, D, blk * m, k_blocks, q_pos0 + r0, SI_BF16, &cc,
                            pl, msg);
@@ -217,8 +225,8 @@ si_status make_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_
         tp.coarse_ws = std::max<int64_t>(tp.coarse_ws, pl.pub.workspace_bytes);
     }
     tp.cidx_off = si::round_up(tp.coarse_ws, 256);
-    tp.cscore_off = tp.cidx_off + si::round_up(qc * k_blocks * 4, 256);
-    tp.cand_off = tp.cscore_off + si::round_up(qc * k_blocks * 4, 256);
+    tp.cscore_off = tp.cidx_off + si::round_up(tp.cqc * k_blocks * 4, 256);
+    tp.cand_off = tp.cscore_off + si::round_up(tp.cqc * k_blocks * 4, 256);
     tp.total = tp.n_chunks == 0 ? 0 : tp.cand_off + qc * tp.cand_stride * 8;
     return SI_OK;
 }
@@ -521,21 +529,27 @@ si_status si_indexer_topk_two_stage(const void* q, si_dtype q_dtype, const void*
         const uint16_t* kbb = static_cast<const uint16_t*>(kb) + b * nb * (int64_t)D;
         for (int64_t c = 0; c < tp.n_chunks; ++c) {
             const int64_t r0 = c * tp.qc, rows = std::min(tp.qc, S - r0);
-            // coarse: the single-stage indexer over the block keys, mask ratio block * m
-            si::PlanInternal pl;
-            st = si::make_plan(1, rows, nb, H, D, block * m, k_blocks, q_pos0 + r0, SI_BF16, &cc,
-                               pl, msg);
-            if (st != SI_OK) return fail(st, "coarse stage: " + msg);
-            const si::Problem P = make_problem(qb + r0 * H * (int64_t)D, kbb, nullptr, wb + r0 * H,
-                                               1, rows, nb, H, block * m, q_pos0 + r0);
-            if ((st = run_indexer(pl, P, k_blocks, si::kOpBf16, cidx, cscore, ws, s)) != SI_OK)
-                return st;
+            // coarse (once per coarse chunk, for all its fine chunks): the single-stage
+            // indexer over the block keys, mask ratio block * m
+            const int64_t c0 = (r0 / tp.cqc) * tp.cqc;
+            if (r0 == c0) {
+                const int64_t crows = std::min(tp.cqc, S - c0);
+                si::PlanInternal pl;
+                st = si::make_plan(1, crows, nb, H, D, block * m, k_blocks, q_pos0 + c0, SI_BF16,
+                                   &cc, pl, msg);
+                if (st != SI_OK) return fail(st, "coarse stage: " + msg);
+                const si::Problem P = make_problem(qb + c0 * H * (int64_t)D, kbb, nullptr,
+                                                   wb + c0 * H, 1, crows, nb, H, block * m,
+                                                   q_pos0 + c0);
+                if ((st = run_indexer(pl, P, k_blocks, si::kOpBf16, cidx, cscore, ws, s)) != SI_OK)
+                    return st;
+            }
             // fine: score the candidates, select the top-k into the output rows
             si::FineArgs a;
             a.q = qb + r0 * H * (int64_t)D;
             a.w = wb + r0 * H;
             a.kc = kcb;
-            a.cidx = cidx;
+            a.cidx = cidx + (r0 - c0) * (int64_t)k_blocks;
             a.cand = cand;
             a.out_idx = out_idx + (b * S + r0) * (int64_t)k;
             a.out_score = out_score + (b * S + r0) * (int64_t)k;

@@ -180,6 +180,28 @@ def test_two_stage_knobs_bit_identical(gpu_lib):
         assert_same(run(gpu_lib, x, kb, spec.m, spec.k, k_blocks=32, **kw), base, str(kw))
 
 
+def test_two_stage_several_coarse_chunks(gpu_lib):
+    """S = 33,000: the coarse indexer runs over coarse chunks of up to 32,768 rows (two
+    here, the second ragged), the fine stage over query chunks inside them.  The output
+    does not depend on how the rows are chunked, and rows on both sides of the coarse
+    boundary match the oracle's two-stage result."""
+    spec = synth.InputSpec(B=1, S=33000, T=2000, H=8, m=16, k=64, seed=36)
+    say("two-stage several coarse chunks", spec)
+    x = synth.make_inputs(spec, device=DEV)
+    kb = gpu_lib.block_keys(x["kc"], 8)
+    base = run(gpu_lib, x, kb, spec.m, spec.k, k_blocks=32)
+    for kw in (dict(query_chunk=96), dict(query_chunk=33000), dict(query_chunk=5000)):
+        assert_same(run(gpu_lib, x, kb, spec.m, spec.k, k_blocks=32, **kw), base, str(kw))
+    rows = [0, 1, 4095, 4096, 32735, 32736, 32767, 32768, 32769, 32999]
+    oi, ov = oracle.two_stage_topk(bits(x["q"]), bits(x["kc"]), x["w"].cpu().numpy(), spec.m,
+                                   spec.k, k_blocks=32, block=8, rows=rows)
+    gin = base[0][0].cpu().numpy()
+    for i, r in enumerate(rows):
+        n = int((oi[0, i] >= 0).sum())
+        assert int((gin[r] >= 0).sum()) == n, r
+        assert len(set(gin[r, :n]) & set(oi[0, i, :n])) >= n - 1, r
+
+
 @pytest.mark.parametrize("T,k,k_blocks,block", [(5, 8, 4, 8), (300, 2048, 2048, 8),
                                                 (900, 1, 1, 8), (700, 700, 3, 32)])
 def test_two_stage_edge_cases(gpu_lib, T, k, k_blocks, block):
