@@ -310,7 +310,7 @@ si_status si_indexer_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, 
  * out_idx / out_score [B, S, k]: the same contract as si_indexer_topk (sorted by score
  * desc, index asc; -1 / -inf padding).  workspace: at least plan.workspace_bytes,
  * 256-byte aligned (coarse workspace and kept block lists of one coarse chunk, fine
- * candidate keys of one query chunk).  The coarse indexer runs once per coarse chunk of
+ * candidate keys and their score ranges of one query chunk).  The coarse indexer runs once per coarse chunk of
  * the largest multiple of query_chunk up to 32768 rows (at least query_chunk), so its
  * query tiles fill the GPU without key partitions; then, per query chunk of it, fine
  * scoring and fine selection.

@@ -175,7 +175,7 @@ si_status run_indexer(const si::PlanInternal& pl, const si::Problem& P, int32_t 
 struct TwoStagePlan {
     int64_t qc, n_chunks, cand_stride;
     int64_t cqc;                 // coarse chunk: query rows of one coarse indexer call
-    int64_t coarse_ws, cidx_off, cscore_off, cand_off, total;
+    int64_t coarse_ws, cidx_off, cscore_off, cand_off, range_off, total;
 };
 
 constexpr int64_t kTwoStageAutoChunk = 4096;
@@ -227,7 +227,8 @@ si_status make_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_
     tp.cidx_off = si::round_up(tp.coarse_ws, 256);
     tp.cscore_off = tp.cidx_off + si::round_up(tp.cqc * k_blocks * 4, 256);
     tp.cand_off = tp.cscore_off + si::round_up(tp.cqc * k_blocks * 4, 256);
-    tp.total = tp.n_chunks == 0 ? 0 : tp.cand_off + qc * tp.cand_stride * 8;
+    tp.range_off = tp.cand_off + si::round_up(qc * tp.cand_stride * 8, 256);
+    tp.total = tp.n_chunks == 0 ? 0 : tp.range_off + qc * 8;
     return SI_OK;
 }
 
@@ -519,6 +520,7 @@ si_status si_indexer_topk_two_stage(const void* q, si_dtype q_dtype, const void*
     int32_t* cidx = reinterpret_cast<int32_t*>(ws + tp.cidx_off);
     float* cscore = reinterpret_cast<float*>(ws + tp.cscore_off);
     uint64_t* cand = reinterpret_cast<uint64_t*>(ws + tp.cand_off);
+    uint32_t* range = reinterpret_cast<uint32_t*>(ws + tp.range_off);
     const int64_t nb = T / block;
     const si_config cc = coarse_config(cfg);
     std::string msg;
@@ -551,6 +553,7 @@ si_status si_indexer_topk_two_stage(const void* q, si_dtype q_dtype, const void*
             a.kc = kcb;
             a.cidx = cidx + (r0 - c0) * (int64_t)k_blocks;
             a.cand = cand;
+            a.range = range;
             a.out_idx = out_idx + (b * S + r0) * (int64_t)k;
             a.out_score = out_score + (b * S + r0) * (int64_t)k;
             a.T = T;

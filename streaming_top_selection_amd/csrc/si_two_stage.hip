@@ -14,6 +14,7 @@
 // heads as MFMA rows (A) and 32 gathered keys as columns (B), with the same
 // v_mfma_f32_32x32x16_bf16 chain over the same d positions per step as score_regs_bf16,
 // then the same head-ordered epilogue acc = fmaf(w_h, max(z_h, 0), acc).
+#include "si_compact.hpp"
 #include "si_kernels.hpp"
 #include "si_sort.hpp"
 
@@ -78,7 +79,8 @@ hipError_t launch_block_keys(const BlockKeyArgs& a, hipStream_t stream) {
 // Candidate position p of row r: p < blk*nk -> key blk * cidx[r][p / blk] + p % blk (the
 // kept blocks, nk = min(k_blocks, complete visible blocks)); then the trailing keys
 // blk*nb .. n-1; past ncand nothing.  Writes the selection key (ord(score), ~index) of
-// each candidate to cand[r][p].
+// each candidate to cand[r][p], and the smallest and largest score image of the row's
+// candidates to range[r] (min > max: no candidate).
 // ---------------------------------------------------------------------------
 constexpr int kFineWaves = 4;
 
@@ -130,6 +132,7 @@ fine_score_kernel(FineArgs A) {
     const float* wrow = A.w + r * H;
 
     const int64_t nchunks = (f.ncand + 63) / 64;
+    uint32_t omin = ~0u, omax = 0u;
     for (int64_t c = 0; c < nchunks; ++c) {
         // B operand: key block kb holds positions 64 c + 32 kb + [0, 32); lane il of each
         // half supplies its column, d = 64 hh + 8 s + [0, 8)
@@ -181,8 +184,17 @@ fine_score_kernel(FineArgs A) {
         }
         const int64_t p = 64 * c + lane;
         const int64_t key = fine_key(A, cidx, f, p);
-        out[p] = key >= 0 ? make_key(canon_zero(acc), (uint32_t)key) : 0ull;
+        const uint64_t sk = key >= 0 ? make_key(canon_zero(acc), (uint32_t)key) : 0ull;
+        out[p] = sk;
+        if (key >= 0) {
+            const uint32_t o = (uint32_t)(sk >> 32);
+            omin = o < omin ? o : omin;
+            omax = o > omax ? o : omax;
+        }
     }
+    omin = wave_min_u32(omin);
+    omax = wave_max_u32(omax);
+    if (lane == 0) *reinterpret_cast<u32x2*>(A.range + 2 * r) = u32x2{omin, omax};
 }
 
 hipError_t launch_fine_score(const FineArgs& a, hipStream_t stream) {
@@ -193,15 +205,22 @@ hipError_t launch_fine_score(const FineArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Fine selection: one wave per row.  The k-th largest candidate key by an exact radix
-// select over the row's keys (read from the workspace), the keys at or above it
-// gathered into LDS, sorted in registers by the bitonic network, written as the row.
+// Fine selection: one wave per row, over the row's keys in the workspace.  With the
+// score range fine scoring recorded, one pass counts the keys per score bin
+// (hist_bin: 256 bins linear in the score between the row's extremes), and the bin d
+// holding the k-th largest key follows; a second pass keeps the keys of higher bins
+// and stages bin d's, whose k - above largest are found by counting larger keys.  When
+// bin d holds more than 64 keys (or the range is empty) the k-th largest key comes from
+// exact radix passes instead and the keys at or above it are kept.  The kept keys
+// (exactly k: keys are unique and non-zero) are sorted in registers by the bitonic
+// network and written as the row.
 // ---------------------------------------------------------------------------
 template <int LE>
 __global__ void __launch_bounds__(64) fine_select_kernel(FineArgs A) {
     constexpr int EPL = 1 << LE;
     __shared__ uint64_t sbuf[64 * EPL];
     __shared__ uint32_t hist[256];
+    __shared__ __attribute__((aligned(16))) uint64_t stage[64];
     const int lane = lane_id();
     const int64_t r = blockIdx.x;
     const int64_t t = A.q_pos0 + r;
@@ -209,17 +228,66 @@ __global__ void __launch_bounds__(64) fine_select_kernel(FineArgs A) {
     const uint64_t* keys = A.cand + r * A.cand_stride;
     const int ncand = (int)f.ncand;
     const int need = min(ncand, A.k);
-    // exactly `need` keys are >= th (keys are unique and non-zero)
-    uint64_t th = 1ull;
-    if (ncand > A.k) th = wave_select_kth(LdsKeys{keys, ncand}, A.k, hist);
-    int pos = 0;
-    for (int base = 0; base < ncand; base += 64) {
-        const int i = base + lane;
-        const uint64_t v = i < ncand ? keys[i] : 0ull;
-        const bool keep = i < ncand && v >= th;
+    // appends the keys of `keep` (one per lane) at pos, in lane order, below cap
+    auto append = [&](bool keep, uint64_t v, uint64_t* dst, int cap, int& pos) {
         const uint64_t bal = __ballot(keep);
-        if (keep) sbuf[pos + __popcll(bal & lanemask_lt())] = v;
+        const int at = pos + __popcll(bal & lanemask_lt());
+        if (keep && at < cap) dst[at] = v;
         pos += __popcll(bal);
+    };
+    int pos = 0;
+    bool done = ncand <= A.k;
+    if (done) {
+        for (int base = 0; base < ncand; base += 64) {
+            const int i = base + lane;
+            append(i < ncand, i < ncand ? keys[i] : 0ull, sbuf, 64 * EPL, pos);
+        }
+    } else {
+        // 256 bins linear in the score between the row's extremes (hist_bin)
+        const u32x2 rg = *reinterpret_cast<const u32x2*>(A.range + 2 * r);
+        const float lo = unord_f32(rg.x), span = unord_f32(rg.y) - lo;
+        if (rg.y > rg.x && span > 0.0f && span < __builtin_inff()) {
+            const float inv = 256.0f / span, off = -(lo * inv);
+            *reinterpret_cast<u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+            wave_sync();
+            for (int base = 0; base < ncand; base += 64) {
+                const int i = base + lane;
+                const uint64_t v = i < ncand ? keys[i] : 0ull;
+                atomicAdd(&hist[hist_bin(key_score(v), inv, off)], i < ncand ? 1u : 0u);
+            }
+            wave_sync();
+            uint32_t above, cntd;
+            const int d = hist_find(hist, A.k, &above, &cntd);
+            wave_sync();
+            if (d >= 0 && cntd <= 64u) {
+                stage[lane] = 0ull;
+                int nd = 0;
+                for (int base = 0; base < ncand; base += 64) {
+                    const int i = base + lane;
+                    const uint64_t v = i < ncand ? keys[i] : 0ull;
+                    const uint32_t bn = hist_bin(key_score(v), inv, off);
+                    append(i < ncand && bn > (uint32_t)d, v, sbuf, 64 * EPL, pos);
+                    append(i < ncand && bn == (uint32_t)d, v, stage, 64, nd);
+                }
+                wave_sync();
+                if (pos == (int)above && nd == (int)cntd) {
+                    const uint64_t th = stage_kth(stage, nd, A.k - pos);
+                    const uint64_t v = stage[lane];
+                    append(lane < nd && v >= th, v, sbuf, 64 * EPL, pos);
+                    done = true;
+                }
+            }
+        }
+        if (!done) {
+            // exactly k keys are >= th
+            const uint64_t th = wave_select_kth(LdsKeys{keys, ncand}, A.k, hist);
+            pos = 0;
+            for (int base = 0; base < ncand; base += 64) {
+                const int i = base + lane;
+                const uint64_t v = i < ncand ? keys[i] : 0ull;
+                append(i < ncand && v >= th, v, sbuf, 64 * EPL, pos);
+            }
+        }
     }
     wave_sync();
     uint64_t x[EPL];
