@@ -202,6 +202,33 @@ def test_two_stage_several_coarse_chunks(gpu_lib):
         assert len(set(gin[r, :n]) & set(oi[0, i, :n])) >= n - 1, r
 
 
+@pytest.mark.parametrize("pattern", ["constant", "two-valued"])
+def test_two_stage_fine_select_fallbacks(gpu_lib, pattern):
+    """Fine selection's radix path: every key equal (a row's candidate scores have no
+    range) or keys alternating between two values (the k-th key's score bin holds far
+    more than 64 candidates).  Ties then decide most of the selection, by index in both
+    stages; the result equals the oracle's two-stage top-k index for index."""
+    spec = synth.InputSpec(B=1, S=1200, T=1200, H=8, m=1, k=100, seed=37)
+    say("two-stage fine-select fallback", pattern)
+    x = synth.make_inputs(spec)
+    kc = x["kc"].clone()
+    if pattern == "constant":
+        kc[0, :] = kc[0, 0]
+    else:
+        kc[0, 0::2] = kc[0, 0]
+        kc[0, 1::2] = kc[0, 1]
+    x = dict(x, kc=kc)
+    xd = {key: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for key, v in x.items()}
+    kb = gpu_lib.block_keys(xd["kc"], 8)
+    gi, gs = run(gpu_lib, xd, kb, spec.m, spec.k, k_blocks=32)
+    rows = [0, 99, 100, 263, 264, 700, spec.S - 1]
+    oi, _ = oracle.two_stage_topk(bits(x["q"]), bits(kc), x["w"].numpy(), spec.m, spec.k,
+                                  k_blocks=32, block=8, rows=rows)
+    gin = gi[0].cpu().numpy()
+    for i, r in enumerate(rows):
+        np.testing.assert_array_equal(gin[r], oi[0, i], err_msg=f"{pattern} row {r}")
+
+
 @pytest.mark.parametrize("T,k,k_blocks,block", [(5, 8, 4, 8), (300, 2048, 2048, 8),
                                                 (900, 1, 1, 8), (700, 700, 3, 32)])
 def test_two_stage_edge_cases(gpu_lib, T, k, k_blocks, block):
