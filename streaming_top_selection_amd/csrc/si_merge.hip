@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A
 // ---- one partition per row, the final selection left to the merge --------------
 // The row's list holds its top k among up to list_max keys (the select stage's
 // threshold keeps it short, but it did not cut it to k).  One wave per row streams the
-// list once, 64 keys a round: the select stage's histogram gives the keep rule
+// list once, 128 keys a round: the select stage's histogram gives the keep rule
 // (KeepRule), so a key above bin d goes straight to the kept set in LDS and a key of
 // bin d to a 64-slot stage, where the k - above largest are found by counting larger
 // keys.  A list the rule does not fit (a query whose histogram was off, or more than
@@ -194,17 +194,28 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
         const KeepRule rl = A.rule[slot0];
         bool fast = rl.d >= 0;
         int base = 0;
+        // two keys per lane and load (slots i + 2 lane, i + 2 lane + 1): the launcher
+        // checks that the list stride holds list_max rounded up to 128 slots
+        auto load2 = [&](int slot, uint64_t& v0, uint64_t& v1) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + slot);
+            v0 = slot < n ? (((uint64_t)w.y << 32) | w.x) : 0ull;
+            v1 = slot + 1 < n ? (((uint64_t)w.w << 32) | w.z) : 0ull;
+        };
         if (fast) {
             sw[lane] = 0ull;
             int nd = 0;
             const uint32_t d = (uint32_t)rl.d;
-#pragma unroll 4
-            for (int i = 0; i < n; i += 64) {
-                const int slot = i + lane;
-                const uint64_t v = slot < n ? src[slot] : 0ull;
-                const uint32_t bn = hist_bin(key_score(v), rl.inv, rl.off);
-                append(slot < n && bn > d, v, kw, 64 * EPL, base);
-                append(slot < n && bn == d, v, sw, 64, nd);
+#pragma unroll 2
+            for (int i = 0; i < n; i += 128) {
+                const int slot = i + 2 * lane;
+                uint64_t v0, v1;
+                load2(slot, v0, v1);
+                const uint32_t b0 = hist_bin(key_score(v0), rl.inv, rl.off);
+                const uint32_t b1 = hist_bin(key_score(v1), rl.inv, rl.off);
+                append(slot < n && b0 > d, v0, kw, 64 * EPL, base);
+                append(slot + 1 < n && b1 > d, v1, kw, 64 * EPL, base);
+                append(slot < n && b0 == d, v0, sw, 64, nd);
+                append(slot + 1 < n && b1 == d, v1, sw, 64, nd);
             }
             const int need = A.k - base;
             // the rule holds for this list (it always does; a list it does not fit goes
@@ -222,11 +233,13 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
             // the keys at or above it (exactly k: keys are unique)
             const uint64_t th = wave_select_kth(LdsKeys{src, n}, A.k, hist[wave]);
             base = 0;
-#pragma unroll 4
-            for (int i = 0; i < n; i += 64) {
-                const int slot = i + lane;
-                const uint64_t v = slot < n ? src[slot] : 0ull;
-                append(slot < n && v >= th, v, kw, 64 * EPL, base);
+#pragma unroll 2
+            for (int i = 0; i < n; i += 128) {
+                const int slot = i + 2 * lane;
+                uint64_t v0, v1;
+                load2(slot, v0, v1);
+                append(slot < n && v0 >= th, v0, kw, 64 * EPL, base);
+                append(slot + 1 < n && v1 >= th, v1, kw, 64 * EPL, base);
             }
         }
         wave_sync();
@@ -302,7 +315,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     // one partition whose list may hold more than k keys: select, then sort
     if (a.list_max > a.k) {
-        if (a.P_chunk != 1 || a.k > 512 || a.CG < a.list_max || a.CG < 512)
+        if (a.P_chunk != 1 || a.k > 512 || a.CG < (a.list_max + 127) / 128 * 128 || a.CG < 512)
             return hipErrorInvalidValue;
         return launch_merge_select_sort<3>(a, rows, stream);
     }
