@@ -228,7 +228,7 @@ si_status make_two_stage_plan(int64_t B, int64_t S, int64_t T, int32_t H, int32_
     tp.cscore_off = tp.cidx_off + si::round_up(tp.cqc * k_blocks * 4, 256);
     tp.cand_off = tp.cscore_off + si::round_up(tp.cqc * k_blocks * 4, 256);
     tp.range_off = tp.cand_off + si::round_up(qc * tp.cand_stride * 8, 256);
-    tp.total = tp.n_chunks == 0 ? 0 : tp.range_off + qc * 8;
+    tp.total = tp.n_chunks == 0 ? 0 : tp.range_off + qc * 64;   // 8 shards x (min, max)
     return SI_OK;
 }
 

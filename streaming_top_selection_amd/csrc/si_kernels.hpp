@@ -107,7 +107,7 @@ struct FineArgs {
     const uint16_t* kc;    // [T, kD] bf16 keys of the batch entry
     const int32_t* cidx;   // [rows, k_blocks] kept block indices (coarse top-k)
     uint64_t* cand;        // [rows, cand_stride] candidate selection keys
-    uint32_t* range;       // [rows, 2] min and max score image (ord) of each row's candidates
+    uint32_t* range;       // [rows, 8, 2] min and max score image (ord) of each (row, key shard)'s candidates
     int32_t* out_idx;      // [rows, k] output rows
     float* out_score;      // [rows, k]
     int64_t T, rows;

@@ -75,14 +75,25 @@ hipError_t launch_block_keys(const BlockKeyArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Fine scoring: one wave per query row, 64 candidate positions per iteration.
-// Candidate position p of row r: p < blk*nk -> key blk * cidx[r][p / blk] + p % blk (the
-// kept blocks, nk = min(k_blocks, complete visible blocks)); then the trailing keys
-// blk*nb .. n-1; past ncand nothing.  Writes the selection key (ord(score), ~index) of
-// each candidate to cand[r][p], and the smallest and largest score image of the row's
-// candidates to range[r] (min > max: no candidate).
+// Fine scoring.  Candidate position p of row r: p < blk*nk -> key blk * cidx[r][p / blk]
+// + p % blk (the kept blocks, nk = min(k_blocks, complete visible blocks)); then the
+// trailing keys blk*nb .. n-1; past ncand nothing.  Writes the selection key (ord(score),
+// ~index) of each candidate to cand[r][p], and the smallest and largest score image of
+// the candidates of each (row, shard) to range[r][shard] (min > max: none).
+//
+// The keys are split into shards of 512-key granules (granule g -> shard g mod 8, a
+// block by its first key), and each row is scored by one wave per shard, in workgroups
+// of consecutive rows of one shard.  Workgroups are handed to the chip's eight
+// accelerator dies (XCDs) in turn, so workgroup i runs on die i mod 8: the shard of
+// workgroup i is i mod 8, and each die gathers keys from one eighth of the key array,
+// which its own L2 can hold (2 MiB of the 16 MiB at S = 262,144) instead of streaming
+// every key from the shared cache.  A wave first lists its shard's kept blocks (and the
+// trailing block) in LDS in rank order, then scores them 64 candidates at a time.
 // ---------------------------------------------------------------------------
 constexpr int kFineWaves = 4;
+constexpr int kFineShards = 8;
+constexpr int kFineGranule = 512;
+constexpr int kFineMaxBlocks = 2048;   // the two-stage plan bounds k_blocks by this
 
 struct FineRow {
     int64_t n, nb, nk, ncand;
@@ -97,24 +108,64 @@ __device__ __forceinline__ FineRow fine_row(const FineArgs& A, int64_t t) {
     return f;
 }
 
-__device__ __forceinline__ int64_t fine_key(const FineArgs& A, const int32_t* cidx,
-                                            const FineRow& f, int64_t p) {
-    if (p < A.blk * f.nk) return (int64_t)cidx[p / A.blk] * A.blk + p % A.blk;
-    if (p < f.ncand) return A.blk * f.nb + (p - A.blk * f.nk);
-    return -1;
+__device__ __forceinline__ int fine_shard(int64_t first_key) {
+    return (int)((first_key / kFineGranule) % kFineShards);
 }
 
 __global__ void __launch_bounds__(kFineWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fine_score_kernel(FineArgs A) {
+    // this wave's blocks: rank in the row's kept list (nk: the trailing block) and the
+    // block index; at most k_blocks + 1 of them
+    __shared__ int32_t sRank[kFineWaves][kFineMaxBlocks + 1];
+    __shared__ int32_t sBlk[kFineWaves][kFineMaxBlocks + 1];
     const int lane = lane_id();
+    const int wave = wave_id();
     const int hh = lane >> 5, il = lane & 31;
-    const int64_t r = (int64_t)blockIdx.x * kFineWaves + wave_id();
-    if (r >= A.rows) return;                          // wave-uniform
+    const int shard = (int)(blockIdx.x % kFineShards);
+    const int64_t r = (int64_t)(blockIdx.x / kFineShards) * kFineWaves + wave;
+    if (r >= A.rows) return;                          // wave-uniform; no barriers below
     const int64_t t = A.q_pos0 + r;                    // absolute position of this row
     const FineRow f = fine_row(A, t);
     const int32_t* cidx = A.cidx + r * A.k_blocks;
     uint64_t* out = A.cand + r * A.cand_stride;
     const int H = A.H;
+    const int blk = A.blk;
+    int32_t* const rank = sRank[wave];
+    int32_t* const blkj = sBlk[wave];
+
+    // this shard's blocks, in rank order
+    int nblk = 0;
+    for (int64_t base = 0; base < f.nk; base += 64) {
+        const int64_t i = base + lane;
+        const int32_t j = i < f.nk ? cidx[i] : 0;
+        const bool mine = i < f.nk && fine_shard((int64_t)j * blk) == shard;
+        const uint64_t bal = __ballot(mine);
+        if (mine) {
+            const int at = nblk + __popcll(bal & lanemask_lt());
+            rank[at] = (int32_t)i;
+            blkj[at] = j;
+        }
+        nblk += __popcll(bal);
+    }
+    const int64_t ntail = f.n - blk * f.nb;            // keys of the trailing block
+    if (ntail > 0 && fine_shard(blk * f.nb) == shard) {
+        if (lane == 0) {
+            rank[nblk] = (int32_t)f.nk;
+            blkj[nblk] = (int32_t)f.nb;
+        }
+        ++nblk;
+    }
+    wave_sync();
+    // slot q of this wave's list: block q / blk, key offset q % blk; its key and the
+    // candidate position it is written to (-1: none)
+    auto slot_key = [&](int64_t q, int64_t* pos) {
+        const int64_t sb = q / blk, o = q - sb * blk;
+        if (sb >= nblk) return (int64_t)-1;
+        const int32_t i = rank[sb];
+        if (i >= f.nk && o >= ntail) return (int64_t)-1;
+        *pos = (int64_t)i * blk + o;
+        return (int64_t)blkj[sb] * blk + o;
+    };
 
     // A operand: heads 32 rb + il of this query, d = 64 hh + 8 s + [0, 8) in step s
     bf16x8 qa[2][8];
@@ -131,15 +182,16 @@ fine_score_kernel(FineArgs A) {
     }
     const float* wrow = A.w + r * H;
 
-    const int64_t nchunks = (f.ncand + 63) / 64;
+    const int64_t nchunks = ((int64_t)nblk * blk + 63) / 64;
     uint32_t omin = ~0u, omax = 0u;
     for (int64_t c = 0; c < nchunks; ++c) {
-        // B operand: key block kb holds positions 64 c + 32 kb + [0, 32); lane il of each
+        // B operand: key block kb holds slots 64 c + 32 kb + [0, 32); lane il of each
         // half supplies its column, d = 64 hh + 8 s + [0, 8)
         bf16x8 kf[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int64_t key = fine_key(A, cidx, f, 64 * c + 32 * kb + il);
+            int64_t pos_unused;
+            const int64_t key = slot_key(64 * c + 32 * kb + il, &pos_unused);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 u32x4 v = {0u, 0u, 0u, 0u};
@@ -158,7 +210,7 @@ fine_score_kernel(FineArgs A) {
 #pragma unroll
                 for (int s = 0; s < 8; ++s) z[rb][kb] = mfma32x32x16(qa[rb][s], kf[kb][s], z[rb][kb]);
             }
-        // Lane il of half hh scores position 64 c + 32 hh + il, i.e. column il of key
+        // Lane il of half hh scores slot 64 c + 32 hh + il, i.e. column il of key
         // block hh.  Register e of lane (il, half g) holds head 32 rb + mfma_row(e, 32 g)
         // of that column, so a lane keeps its own half's heads of block hh and receives
         // the other half's from lane ^ 32.
@@ -182,11 +234,11 @@ fine_score_kernel(FineArgs A) {
                 acc = __builtin_fmaf(wrow[h], __builtin_fmaxf(zz, 0.0f), acc);
             }
         }
-        const int64_t p = 64 * c + lane;
-        const int64_t key = fine_key(A, cidx, f, p);
-        const uint64_t sk = key >= 0 ? make_key(canon_zero(acc), (uint32_t)key) : 0ull;
-        out[p] = sk;
+        int64_t p = 0;
+        const int64_t key = slot_key(64 * c + lane, &p);
         if (key >= 0) {
+            const uint64_t sk = make_key(canon_zero(acc), (uint32_t)key);
+            out[p] = sk;
             const uint32_t o = (uint32_t)(sk >> 32);
             omin = o < omin ? o : omin;
             omax = o > omax ? o : omax;
@@ -194,12 +246,14 @@ fine_score_kernel(FineArgs A) {
     }
     omin = wave_min_u32(omin);
     omax = wave_max_u32(omax);
-    if (lane == 0) *reinterpret_cast<u32x2*>(A.range + 2 * r) = u32x2{omin, omax};
+    if (lane == 0)
+        *reinterpret_cast<u32x2*>(A.range + 2 * (r * kFineShards + shard)) = u32x2{omin, omax};
 }
 
 hipError_t launch_fine_score(const FineArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    const int64_t grid = (a.rows + kFineWaves - 1) / kFineWaves;
+    if (a.k_blocks > kFineMaxBlocks) return hipErrorInvalidValue;
+    const int64_t grid = (a.rows + kFineWaves - 1) / kFineWaves * kFineShards;
     hipLaunchKernelGGL(fine_score_kernel, dim3((unsigned)grid), dim3(kFineWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -244,7 +298,14 @@ __global__ void __launch_bounds__(64) fine_select_kernel(FineArgs A) {
         }
     } else {
         // 256 bins linear in the score between the row's extremes (hist_bin)
-        const u32x2 rg = *reinterpret_cast<const u32x2*>(A.range + 2 * r);
+        // the row's score range: the extremes over the shards' ranges
+        u32x2 rg = {~0u, 0u};
+#pragma unroll
+        for (int x = 0; x < kFineShards; ++x) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(A.range + 2 * (r * kFineShards + x));
+            rg.x = min(rg.x, v.x);
+            rg.y = max(rg.y, v.y);
+        }
         const float lo = unord_f32(rg.x), span = unord_f32(rg.y) - lo;
         if (rg.y > rg.x && span > 0.0f && span < __builtin_inff()) {
             const float inv = 256.0f / span, off = -(lo * inv);
