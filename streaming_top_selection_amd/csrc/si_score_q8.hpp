@@ -198,9 +198,14 @@ __device__ __forceinline__ void score_regs_q8(const Problem& P, int64_t b, int64
 
     // the skewed pipeline of score_regs_bf16: the MFMAs of block X + LA run beside the
     // epilogue of block X; head h+1's operands are read in step h; one barrier per two
-    // heads publishes the next two staged tiles
-    constexpr int ZR = (KB == 1) ? 2 : ((KB % 3 == 0) ? 3 : 2);
-    constexpr int LA = ZR - 1;
+    // heads publishes the next two staged tiles.  A block's chain here is two MFMAs
+    // (against eight bf16 ones), short enough that with one block of lookahead the
+    // epilogue would read results still in flight and stall on the MFMA result hazard;
+    // two blocks of lookahead (three of four accumulator slots live) hide it.  With
+    // fewer than four blocks a head's operands, read one block ahead, would not be in
+    // registers in time for a chain two blocks ahead, so those shapes keep one.
+    constexpr int LA = (KB >= 4) ? 2 : 1;
+    constexpr int ZR = (LA == 2) ? 4 : ((KB % 3 == 0) ? 3 : 2);
     static_assert((kQBuf * KB) % ZR == 0, "slots must repeat every group of 8 heads");
     static_assert(LA <= KB, "lookahead stays within the next head");
     f32x16 z[ZR];
