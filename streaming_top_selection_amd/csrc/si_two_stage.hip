@@ -180,7 +180,15 @@ fine_score_kernel(FineArgs A) {
             qa[rb][s] = __builtin_bit_cast(bf16x8, v);
         }
     }
+    // the row's head weights, read once (0 past H: those heads' scores are exact zeros,
+    // their terms add +0 as in the single-stage tile)
     const float* wrow = A.w + r * H;
+    float wr[64];
+#pragma unroll
+    for (int h = 0; h < 64; ++h) {
+        const float wv = wrow[min(h, H - 1)];
+        wr[h] = h < H ? wv : 0.0f;
+    }
 
     const int64_t nchunks = ((int64_t)nblk * blk + 63) / 64;
     uint32_t omin = ~0u, omax = 0u;
@@ -212,27 +220,27 @@ fine_score_kernel(FineArgs A) {
             }
         // Lane il of half hh scores slot 64 c + 32 hh + il, i.e. column il of key
         // block hh.  Register e of lane (il, half g) holds head 32 rb + mfma_row(e, 32 g)
-        // of that column, so a lane keeps its own half's heads of block hh and receives
-        // the other half's from lane ^ 32.
-        float own[2][16], oth[2][16];
+        // of that column.  Swapping the upper half of block 0's registers with the lower
+        // half of block 1's (v_permlane32_swap) leaves every lane with both head groups
+        // of its own block: g0 holds the heads of group 0, g1 those of group 1.
+        float g0[2][16], g1[2][16];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                own[rb][e] = hh ? z[rb][1][e] : z[rb][0][e];
-                const float send = hh ? z[rb][0][e] : z[rb][1][e];
-                oth[rb][e] = __shfl_xor(send, 32);
+                const auto sw = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(z[rb][0][e]), __float_as_uint(z[rb][1][e]), false, false);
+                g0[rb][e] = __uint_as_float(sw[0]);
+                g1[rb][e] = __uint_as_float(sw[1]);
             }
-        // acc = fmaf(w_h, max(z_h, 0), acc) for h = 0 .. H-1 from +0, as in the tile
+        // acc = fmaf(w_h, max(z_h, 0), acc) for h = 0 .. 63 from +0, as in the tile
         float acc = 0.0f;
 #pragma unroll
         for (int h = 0; h < 64; ++h) {
-            if (h < H) {
-                const int rb = h >> 5, hl = h & 31;
-                const int e = 4 * (hl >> 3) + (hl & 3);
-                const float zz = (((hl >> 2) & 1) == hh) ? own[rb][e] : oth[rb][e];
-                acc = __builtin_fmaf(wrow[h], __builtin_fmaxf(zz, 0.0f), acc);
-            }
+            const int rb = h >> 5, hl = h & 31;
+            const int e = 4 * (hl >> 3) + (hl & 3);
+            const float zz = ((hl >> 2) & 1) ? g1[rb][e] : g0[rb][e];
+            acc = __builtin_fmaf(wr[h], __builtin_fmaxf(zz, 0.0f), acc);
         }
         int64_t p = 0;
         const int64_t key = slot_key(64 * c + lane, &p);
