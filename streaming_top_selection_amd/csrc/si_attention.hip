@@ -15,13 +15,14 @@
 //   O^T[D x 32 heads]      += KV^T[D x 32] * P^T[32 x 32] (weights rounded to bf16)
 // The score layout puts one head per lane column, so a head's maximum and sum need
 // one exchange with lane ^ 32 and the rescale of O is a per-lane multiply.  The next
-// block's rows are loaded into registers while the current block is computed.
+// two blocks' rows are loaded into registers while the current block is computed
+// (the kernel is compiled per wave count, so the gather loops unroll and the staged
+// rows stay in registers).
 #include "si_kernels.hpp"
 
 namespace si {
 
 constexpr int kAttnKeys = 32;                  // selected entries per block
-constexpr int kAttnMaxWaves = 4;               // up to 128 heads
 constexpr int kKvtStride = 36;                 // bf16 per transposed row (32 + 4 pad)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -34,13 +35,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return ra | (rb << 16);
 }
 
-__global__ void __launch_bounds__(kAttnMaxWaves * 64) sparse_attention_kernel(AttnArgs A) {
+template <int NW>
+__global__ void __launch_bounds__(NW * 64) sparse_attention_kernel(AttnArgs A) {
     __shared__ __attribute__((aligned(16))) uint16_t kvs[kAttnKeys * kD];        // 8 KiB
     __shared__ __attribute__((aligned(16))) uint16_t kvt[kD * kKvtStride];       // 9 KiB
     const int lane = lane_id();
     const int wave = wave_id();
     const int hh = lane >> 5, il = lane & 31;
-    const int nthreads = (int)blockDim.x;
+    constexpr int nthreads = NW * 64;
     const int tid = threadIdx.x;
     const int64_t bt = blockIdx.x;                 // b * S + t
     const int64_t b = bt / A.S;
@@ -82,9 +84,10 @@ __global__ void __launch_bounds__(kAttnMaxWaves * 64) sparse_attention_kernel(At
 
     // gather: piece id = it * nthreads + tid covers key r = id / 16, d = 8 (id % 16) + [0, 8)
     constexpr int npieces = kAttnKeys * (kD / 8);
-    const int per_thread = (npieces + nthreads - 1) / nthreads;   // 8, 4, 3 or 2
-    u32x4 pre[8];
-    auto load_block = [&](int blk) {
+    constexpr int per_thread = (npieces + nthreads - 1) / nthreads;   // 8, 4, 3 or 2
+    u32x4 pre[2][8];      // two blocks in flight
+    auto load_block = [&](int blk, u32x4 (&pr)[8]) {
+#pragma unroll
         for (int it = 0; it < per_thread; ++it) {
             const int id = it * nthreads + tid;
             if (id >= npieces) break;
@@ -92,16 +95,17 @@ __global__ void __launch_bounds__(kAttnMaxWaves * 64) sparse_attention_kernel(At
             const int j = blk * kAttnKeys + r;
             u32x4 v = {0u, 0u, 0u, 0u};
             if (j < n_sel) v = *reinterpret_cast<const u32x4*>(kvb + (int64_t)sel[j] * kD + 8 * c);
-            pre[it] = v;
+            pr[it] = v;
         }
     };
-    auto store_block = [&]() {
+    auto store_block = [&](const u32x4 (&pr)[8]) {
+#pragma unroll
         for (int it = 0; it < per_thread; ++it) {
             const int id = it * nthreads + tid;
             if (id >= npieces) break;
             const int r = id >> 4, c = id & 15;
-            *reinterpret_cast<u32x4*>(&kvs[(16 * r + (c ^ (r & 15))) * 8]) = pre[it];
-            const uint32_t wd[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
+            *reinterpret_cast<u32x4*>(&kvs[(16 * r + (c ^ (r & 15))) * 8]) = pr[it];
+            const uint32_t wd[4] = {pr[it].x, pr[it].y, pr[it].z, pr[it].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 kvt[(8 * c + 2 * e) * kKvtStride + r] = (uint16_t)(wd[e] & 0xFFFFu);
@@ -111,12 +115,17 @@ __global__ void __launch_bounds__(kAttnMaxWaves * 64) sparse_attention_kernel(At
     };
 
     const int nblocks = (n_sel + kAttnKeys - 1) / kAttnKeys;
-    if (nblocks > 0) load_block(0);
+    if (nblocks > 0) load_block(0, pre[0]);
+    if (nblocks > 1) load_block(1, pre[1]);
     for (int blk = 0; blk < nblocks; ++blk) {
         __syncthreads();                              // the previous block's reads are done
-        store_block();
+        // blocks blk (slot blk % 2) and blk + 1 are in flight; store blk, then refill
+        // its slot with blk + 2
+        if (blk & 1) store_block(pre[1]); else store_block(pre[0]);
         __syncthreads();                              // this block is in LDS
-        if (blk + 1 < nblocks) load_block(blk + 1);   // in flight during the compute
+        if (blk + 2 < nblocks) {
+            if (blk & 1) load_block(blk + 2, pre[1]); else load_block(blk + 2, pre[0]);
+        }
 
         // S^T = KV * qa^T: A = key rows (lane il: key il, d = 64 hh + 8 s + [0, 8))
         f32x16 z;
@@ -196,7 +205,14 @@ hipError_t launch_sparse_attention(const AttnArgs& a, hipStream_t stream) {
     const int64_t grid = a.B * a.S;
     if (grid <= 0) return hipSuccess;
     const int waves = (a.HA + 31) / 32;
-    hipLaunchKernelGGL(sparse_attention_kernel, dim3((unsigned)grid), dim3(64 * waves), 0, stream, a);
+    const dim3 g((unsigned)grid);
+    switch (waves) {
+        case 1: hipLaunchKernelGGL(sparse_attention_kernel<1>, g, dim3(64), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(sparse_attention_kernel<2>, g, dim3(128), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(sparse_attention_kernel<3>, g, dim3(192), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(sparse_attention_kernel<4>, g, dim3(256), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
