@@ -319,10 +319,20 @@ __global__ void __launch_bounds__(64) fine_select_kernel(FineArgs A) {
             const float inv = 256.0f / span, off = -(lo * inv);
             *reinterpret_cast<u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
             wave_sync();
-            for (int base = 0; base < ncand; base += 64) {
-                const int i = base + lane;
-                const uint64_t v = i < ncand ? keys[i] : 0ull;
-                atomicAdd(&hist[hist_bin(key_score(v), inv, off)], i < ncand ? 1u : 0u);
+            // eight keys per lane in flight per round (one load and wait at a time left
+            // each pass latency-bound)
+            for (int base = 0; base < ncand; base += 8 * 64) {
+                uint64_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = base + 64 * u + lane;
+                    v[u] = i < ncand ? keys[i] : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = base + 64 * u + lane;
+                    atomicAdd(&hist[hist_bin(key_score(v[u]), inv, off)], i < ncand ? 1u : 0u);
+                }
             }
             wave_sync();
             uint32_t above, cntd;
@@ -331,12 +341,20 @@ __global__ void __launch_bounds__(64) fine_select_kernel(FineArgs A) {
             if (d >= 0 && cntd <= 64u) {
                 stage[lane] = 0ull;
                 int nd = 0;
-                for (int base = 0; base < ncand; base += 64) {
-                    const int i = base + lane;
-                    const uint64_t v = i < ncand ? keys[i] : 0ull;
-                    const uint32_t bn = hist_bin(key_score(v), inv, off);
-                    append(i < ncand && bn > (uint32_t)d, v, sbuf, 64 * EPL, pos);
-                    append(i < ncand && bn == (uint32_t)d, v, stage, 64, nd);
+                for (int base = 0; base < ncand; base += 8 * 64) {
+                    uint64_t v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int i = base + 64 * u + lane;
+                        v[u] = i < ncand ? keys[i] : 0ull;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int i = base + 64 * u + lane;
+                        const uint32_t bn = hist_bin(key_score(v[u]), inv, off);
+                        append(i < ncand && bn > (uint32_t)d, v[u], sbuf, 64 * EPL, pos);
+                        append(i < ncand && bn == (uint32_t)d, v[u], stage, 64, nd);
+                    }
                 }
                 wave_sync();
                 if (pos == (int)above && nd == (int)cntd) {
