@@ -146,6 +146,8 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_sort_kernel(MergeArgs A
 // memory and is streamed again.  The k kept keys are read back from LDS in the sort
 // layout, sorted in registers (64*EPL >= k) and written.  A list of at most k keys is
 // sorted directly.  Few registers per wave, so many waves per SIMD hide the loads.
+constexpr int kMergeRounds = 4;   // list rounds of 128 slots loaded ahead of use
+
 template <int LE>
 __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(MergeArgs A) {
     constexpr int EPL = 1 << LE;
@@ -196,8 +198,11 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
         int base = 0;
         // two keys per lane and load (slots i + 2 lane, i + 2 lane + 1): the launcher
         // checks that the list stride holds list_max rounded up to 128 slots
+        // (a slot past the list's last 128-slot round reads that round's last pair
+        // instead, so loads need no branch; its keys are dropped as past n)
+        const int lim = (n + 127) / 128 * 128 - 2;
         auto load2 = [&](int slot, uint64_t& v0, uint64_t& v1) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(src + slot);
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + min(slot, lim));
             v0 = slot < n ? (((uint64_t)w.y << 32) | w.x) : 0ull;
             v1 = slot + 1 < n ? (((uint64_t)w.w << 32) | w.z) : 0ull;
         };
@@ -205,17 +210,22 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
             sw[lane] = 0ull;
             int nd = 0;
             const uint32_t d = (uint32_t)rl.d;
-#pragma unroll 2
-            for (int i = 0; i < n; i += 128) {
-                const int slot = i + 2 * lane;
-                uint64_t v0, v1;
-                load2(slot, v0, v1);
-                const uint32_t b0 = hist_bin(key_score(v0), rl.inv, rl.off);
-                const uint32_t b1 = hist_bin(key_score(v1), rl.inv, rl.off);
-                append(slot < n && b0 > d, v0, kw, 64 * EPL, base);
-                append(slot + 1 < n && b1 > d, v1, kw, 64 * EPL, base);
-                append(slot < n && b0 == d, v0, sw, 64, nd);
-                append(slot + 1 < n && b1 == d, v1, sw, 64, nd);
+            // rounds of 128 slots, four loaded before any is used (one load and wait at
+            // a time left the stream latency-bound)
+            for (int i = 0; i < n; i += kMergeRounds * 128) {
+                uint64_t v[kMergeRounds][2];
+#pragma unroll
+                for (int u = 0; u < kMergeRounds; ++u) load2(i + 128 * u + 2 * lane, v[u][0], v[u][1]);
+#pragma unroll
+                for (int u = 0; u < kMergeRounds; ++u) {
+                    const int slot = i + 128 * u + 2 * lane;
+                    const uint32_t b0 = hist_bin(key_score(v[u][0]), rl.inv, rl.off);
+                    const uint32_t b1 = hist_bin(key_score(v[u][1]), rl.inv, rl.off);
+                    append(slot < n && b0 > d, v[u][0], kw, 64 * EPL, base);
+                    append(slot + 1 < n && b1 > d, v[u][1], kw, 64 * EPL, base);
+                    append(slot < n && b0 == d, v[u][0], sw, 64, nd);
+                    append(slot + 1 < n && b1 == d, v[u][1], sw, 64, nd);
+                }
             }
             const int need = A.k - base;
             // the rule holds for this list (it always does; a list it does not fit goes
@@ -233,13 +243,16 @@ __global__ void __launch_bounds__(kSortWaves * 64) merge_select_sort_kernel(Merg
             // the keys at or above it (exactly k: keys are unique)
             const uint64_t th = wave_select_kth(LdsKeys{src, n}, A.k, hist[wave]);
             base = 0;
-#pragma unroll 2
-            for (int i = 0; i < n; i += 128) {
-                const int slot = i + 2 * lane;
-                uint64_t v0, v1;
-                load2(slot, v0, v1);
-                append(slot < n && v0 >= th, v0, kw, 64 * EPL, base);
-                append(slot + 1 < n && v1 >= th, v1, kw, 64 * EPL, base);
+            for (int i = 0; i < n; i += kMergeRounds * 128) {
+                uint64_t v[kMergeRounds][2];
+#pragma unroll
+                for (int u = 0; u < kMergeRounds; ++u) load2(i + 128 * u + 2 * lane, v[u][0], v[u][1]);
+#pragma unroll
+                for (int u = 0; u < kMergeRounds; ++u) {
+                    const int slot = i + 128 * u + 2 * lane;
+                    append(slot < n && v[u][0] >= th, v[u][0], kw, 64 * EPL, base);
+                    append(slot + 1 < n && v[u][1] >= th, v[u][1], kw, 64 * EPL, base);
+                }
             }
         }
         wave_sync();
