@@ -387,27 +387,40 @@ select_kernel(SelectArgs A) {
 
     int sub = 0;
     int key_tiles = 0;                     // key tiles done in this partition
-    for (int64_t key0 = key_lo; key0 < key_hi; key0 += RT) {
-        f32x16 acc[KB];
-        score_tile<NWAVE, KB, OP>(P, b, row0, rows_valid, key0, key_hi, L, Q, acc);
+    // score and filter one register tile of KBT key blocks per wave
+    auto score_filter = [&](auto kbt, int64_t key0) {
+        constexpr int KBT = decltype(kbt)::value;
+        f32x16 acc[KBT];
+        score_tile<NWAVE, KBT, OP>(P, b, row0, rows_valid, key0, key_hi, L, Q, acc);
 
-        const int64_t kbase = key0 + (int64_t)wave * KB * kMB;
+        const int64_t kbase = key0 + (int64_t)wave * KBT * kMB;
         uint64_t* const cand_tile = A.cand + slot0 * CGS;
         if (key0 == key_lo) {
             // the histogram scale of each query: the extremes of its first register tile
-            row_extremes<KB>(acc, kbase, sN, sOmin, sOmax);
+            row_extremes<KBT>(acc, kbase, sN, sOmin, sOmax);
             __syncthreads();
             if (tid < kTQ)
                 row_hist_params(sOmin[tid], sOmax[tid], &sLo[tid], &sWid[tid], &sInv[tid],
                                 &sOff[tid]);
             __syncthreads();
         }
-        if (kbase + KB * kMB <= all_visible)
-            filter_append<KB, CG, false>(acc, kbase, sThf, sN, sCnt, sInv, sOff, sRowHist,
-                                         cand_tile, row_stride);
+        if (kbase + KBT * kMB <= all_visible)
+            filter_append<KBT, CG, false>(acc, kbase, sThf, sN, sCnt, sInv, sOff, sRowHist,
+                                          cand_tile, row_stride);
         else
-            filter_append<KB, CG, true>(acc, kbase, sThf, sN, sCnt, sInv, sOff, sRowHist,
-                                        cand_tile, row_stride);
+            filter_append<KBT, CG, true>(acc, kbase, sThf, sN, sCnt, sInv, sOff, sRowHist,
+                                         cand_tile, row_stride);
+    };
+    for (int64_t key0 = key_lo; key0 < key_hi; key0 += RT) {
+        // a last register tile that needs at most half its keys is scored at half width
+        // (the keys past the visible end would only be zero operands)
+        if constexpr (KB == 4 && NSUB == 1) {
+            if (key_hi - key0 <= RT / 4) score_filter(std::integral_constant<int, 1>{}, key0);
+            else if (key_hi - key0 <= RT / 2) score_filter(std::integral_constant<int, 2>{}, key0);
+            else score_filter(std::integral_constant<int, KB>{}, key0);
+        } else {
+            score_filter(std::integral_constant<int, KB>{}, key0);
+        }
 
         // ---- compaction: keep room for one more key tile; exact top-k at the end ----
         ++sub;
